@@ -1,0 +1,409 @@
+"""fp64 CPU oracle for weight-absorbed Multi-Head Latent Attention (MLA).
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import or call this module. The HIP library never routes
+through it and it imports nothing from the HIP library.
+
+It computes MLA the slow, obviously-correct way: every bf16 input is widened
+to float64, per-head keys and values are expanded explicitly from the latent
+c_KV, the decoupled RoPE key is concatenated to every head's key, and a plain
+softmax attention is taken. Dimensions are read from the array shapes, so the
+same code runs on tiny brute-force shapes and on the DeepSeek-V2 shapes.
+
+Sources (page title, section):
+  [P1] "论文复现工坊 No.4：从零复现 DeepSeek-V2/V3 多头潜在注意力 MLA"
+       (m.xxqk.cn): section 1 (latent c_KV, decoupled RoPE, cache of
+       d_c + d_R per token), section 2 (the PyTorch module: split of the
+       wkv_b output into k_nope and v per head, k_rope broadcast to all heads,
+       scale = 1/sqrt(qk_nope_head_dim + qk_rope_head_dim), softmax in float),
+       section 4 (absorption: Q_absorbed = Q W_UK^T scored against c^KV).
+  [P3] "淺析DeepSeek多頭潛在注意力機制（MLA）" (itdecent.cn): "大模型的整體推理過程"
+       (decode appends the new token's K/V, then attends over all N+1 tokens;
+       masked self-attention), "MLA的數學原理" (k_i = c_i W_k; the product
+       x_t (W_q W_k^T) c_i^T), "MLA與ROPE的融合" (RoPE angle
+       theta_i = 10000^(-2i/d), block-diagonal R_m with R_m R_n^T = R_{m-n};
+       score of concatenated parts = sum of the part scores; a 64-dim RoPE
+       key shared by all heads).
+  [P4] "Multi-Head Latent Attention: DeepSeek V2/V3 工程视角" (xuquant.com),
+       section 一 (n_h = 128, d_c = 512, d_h^R = 64, 576 elements per token).
+
+Readings where the pages leave a step open (each is also listed in the design notes):
+  * RoPE pairs are interleaved (x_{2i}, x_{2i+1}) and rotate by pos * theta_i,
+    theta_i = 10000^(-2i/d_R) with d = d_R (the decoupled part only).
+  * The cache row is [c_KV | k_R] (the split order of the module's wkv_a output).
+  * W_UK[h] and W_UV[h] are stored [d_out, d_c] (the nn.Linear row layout of
+    wkv_b after its per-head split): k_nope = W_UK[h] c, v = W_UV[h] c.
+  * Decode: the query is the sequence's last token (position L-1) and sees
+    keys 0..L-1. Prefill: query at position p sees keys 0..p (causal).
+  * lse is the natural-log log-sum-exp of the scaled scores.
+  * bf16 rounding is round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+ROPE_THETA = 10000.0
+
+
+# ----------------------------------------------------------------------------- bf16
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float64 exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 bit patterns, round-to-nearest-even, by integer surgery on the
+    float64 encoding: keep 7 of the 52 stored mantissa bits and round on the 45 dropped bits.
+
+    Zeros and normal bf16 results are handled; anything else (NaN, inf, a bf16 subnormal
+    or overflow) raises, since the method never produces such values from its inputs.
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    u = x.view(np.uint64)
+    sign = (u >> np.uint64(63)).astype(np.uint32)
+    exp = ((u >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
+    mant = (u & np.uint64((1 << 52) - 1))
+    keep = (mant >> np.uint64(45)).astype(np.int64)              # 7 mantissa bits
+    rest = (mant & np.uint64((1 << 45) - 1)).astype(np.int64)
+    half = 1 << 44
+    up = (rest > half) | ((rest == half) & ((keep & 1) == 1))
+    ebf = exp - 1023 + 127
+    combined = (ebf << 7) + keep + up.astype(np.int64)            # carry ripples into the exponent
+    zero = (exp == 0) & (mant == 0)
+    bad = (~zero) & ((exp == 0x7FF) | (ebf <= 0) | (combined >= (0xFF << 7)))
+    if np.any(bad):
+        raise ValueError("bf16 rounding: value outside the normal bf16 range")
+    out = np.where(zero, 0, combined).astype(np.uint32) | (sign << 15)
+    return out.astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def rope_inv_freq(d_rope: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """theta_i = base^(-2i/d) for i = 0 .. d/2-1 ([P3] "MLA與ROPE的融合"), d = d_R."""
+    i = np.arange(d_rope // 2, dtype=np.float64)
+    return theta ** (-2.0 * i / d_rope)
+
+
+def rope_rotate(x: np.ndarray, pos, theta: float = ROPE_THETA) -> np.ndarray:
+    """Apply R_pos to the last axis of x (float64): pair i = (x_{2i}, x_{2i+1}) turns by pos*theta_i.
+
+    `pos` broadcasts against x.shape[:-1].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(d, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    even, odd = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
+    out[..., 0::2] = even * c - odd * s
+    out[..., 1::2] = even * s + odd * c
+    return out
+
+
+# ----------------------------------------------------------------------------- cache
+
+def slot_of(block_table: Optional[np.ndarray], max_blocks: int, block_size: int, seq: int, pos: int):
+    """(physical block, row in block) holding token `pos` of sequence `seq`.
+
+    With no table the layout is contiguous: logical block i of sequence b is physical block
+    b * max_blocks + i.
+    """
+    blk = pos // block_size
+    phys = seq * max_blocks + blk if block_table is None else int(block_table[seq, blk])
+    return phys, pos % block_size
+
+
+def rope_append(cache: np.ndarray, block_table, max_blocks: int, token_seq, token_pos,
+                c_kv: np.ndarray, k_rope: np.ndarray, q_rope: Optional[np.ndarray] = None,
+                theta: float = ROPE_THETA):
+    """Write rows [c_KV | R_pos k_R] (bf16) into the paged cache; rotate q_R at the same positions.
+
+    cache: [num_blocks, block_size, d_c + d_R] uint16 (modified copy is returned).
+    c_kv: [T, d_c], k_rope: [T, d_R], q_rope: [T, n_h, d_R] (uint16, un-rotated) or None.
+    Returns (cache, q_rope_rotated or None), both bf16 bit patterns.
+    ([P1] section 1 and section 2 split order; [P3] "MLA與ROPE的融合".)
+    """
+    cache = cache.copy()
+    nb, bs, row = cache.shape
+    d_c = c_kv.shape[1]
+    d_r = k_rope.shape[1]
+    assert row == d_c + d_r
+    token_seq = np.asarray(token_seq)
+    token_pos = np.asarray(token_pos)
+    k_rot = f64_to_bf16(rope_rotate(bf16_to_f64(k_rope), token_pos, theta))
+    for t in range(token_seq.shape[0]):
+        phys, r = slot_of(block_table, max_blocks, bs, int(token_seq[t]), int(token_pos[t]))
+        cache[phys, r, :d_c] = c_kv[t]
+        cache[phys, r, d_c:] = k_rot[t]
+    q_rot = None
+    if q_rope is not None:
+        q_rot = f64_to_bf16(rope_rotate(bf16_to_f64(q_rope), np.asarray(token_pos)[:, None], theta))
+    return cache, q_rot
+
+
+def gather_rows(cache: np.ndarray, block_table, max_blocks: int, seq: int, length: int) -> np.ndarray:
+    """The first `length` cached rows of sequence `seq`, widened to float64: [length, d_c + d_R]."""
+    nb, bs, row = cache.shape
+    out = np.empty((length, row), dtype=np.float64)
+    for blk in range((length + bs - 1) // bs):
+        phys, _ = slot_of(block_table, max_blocks, bs, seq, blk * bs)
+        n = min(bs, length - blk * bs)
+        out[blk * bs: blk * bs + n] = bf16_to_f64(cache[phys, :n])
+    return out
+
+
+# ----------------------------------------------------------------------------- attention pieces
+
+def softmax_scale(d_nope: int, d_rope: int) -> float:
+    """1/sqrt(qk_nope_head_dim + qk_rope_head_dim) ([P1] section 2)."""
+    return 1.0 / math.sqrt(d_nope + d_rope)
+
+
+def softmax_lse(s: np.ndarray, axis: int = -1):
+    """Row softmax of float64 scores with the max subtracted, and the natural-log log-sum-exp.
+
+    Rows that are entirely -inf (no visible key) get p = 0 and lse = -inf.
+    """
+    m = np.max(s, axis=axis, keepdims=True)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    e = np.exp(s - m_safe)
+    z = np.sum(e, axis=axis, keepdims=True)
+    p = np.where(finite, e / np.where(z > 0, z, 1.0), 0.0)
+    lse = np.where(finite, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    return p, np.squeeze(lse, axis=axis)
+
+
+def expand_kv(c: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray):
+    """Per-head keys and values from the latent: K[h,t] = W_UK[h] c_t, V[h,t] = W_UV[h] c_t.
+
+    c: [L, d_c]; w_uk: [H, d_nope, d_c]; w_uv: [H, d_v, d_c] -> K [H, L, d_nope], V [H, L, d_v].
+    ([P1] section 2: wkv_b then view/split into k_nope and v; [P3] "MLA的數學原理": k_i = c_i W_k.)
+    """
+    K = np.matmul(c[None, :, :], np.swapaxes(w_uk, 1, 2))
+    V = np.matmul(c[None, :, :], np.swapaxes(w_uv, 1, 2))
+    return K, V
+
+
+def _head_chunk(length: int, d: int) -> int:
+    return max(1, int((1 << 26) // max(1, length * d)))
+
+
+def _as_list(x, n):
+    return list(range(n)) if x is None else [int(v) for v in x]
+
+
+# ----------------------------------------------------------------------------- decode, expanded form
+
+def decode(cache, block_table, max_blocks, seq_lens, q_nope, q_rope, w_uk, w_uv,
+           seqs: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None):
+    """Decode attention in expanded (non-absorbed) form, float64.
+
+    q_nope [B, H, d_nope], q_rope [B, H, d_R] (already rotated), bf16 bit patterns.
+    For every head: k_full[t] = [W_UK[h] c_t | k_R,t], v[t] = W_UV[h] c_t,
+    s_t = scale * [q_nope | q_R] . k_full[t] over t < L_b, p = softmax(s), out = sum_t p_t v[t].
+    ([P1] section 2 forward; [P3] "大模型的整體推理過程": the query attends to all N+1 cached tokens.)
+    Returns out [B, H, d_v] and lse [B, H]; rows of unselected (seq, head) are NaN.
+    """
+    B, H, d_nope = q_nope.shape
+    d_r = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    scale = softmax_scale(d_nope, d_r)
+    out = np.full((B, H, d_v), np.nan)
+    lse = np.full((B, H), np.nan)
+    wk = bf16_to_f64(w_uk)
+    wv = bf16_to_f64(w_uv)
+    qn = bf16_to_f64(q_nope)
+    qr = bf16_to_f64(q_rope)
+    hs = _as_list(heads, H)
+    for b in _as_list(seqs, B):
+        L = int(seq_lens[b])
+        if L == 0:
+            out[b, hs] = 0.0
+            lse[b, hs] = -np.inf
+            continue
+        rows = gather_rows(cache, block_table, max_blocks, b, L)
+        c, kr = rows[:, :d_c], rows[:, d_c:]
+        step = _head_chunk(L, d_nope + d_v)
+        for i in range(0, len(hs), step):
+            hh = hs[i:i + step]
+            K, V = expand_kv(c, wk[hh], wv[hh])                          # [h, L, *]
+            k_full = np.concatenate([K, np.broadcast_to(kr, (len(hh),) + kr.shape)], axis=2)
+            q_full = np.concatenate([qn[b, hh], qr[b, hh]], axis=1)      # [h, d_nope + d_R]
+            s = np.einsum("hld,hd->hl", k_full, q_full) * scale
+            p, l = softmax_lse(s)
+            out[b, hh] = np.einsum("hl,hld->hd", p, V)
+            lse[b, hh] = l
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- chunked prefill, expanded form
+
+def causal_visible(pos: np.ndarray, n_keys: int) -> np.ndarray:
+    """visible[j, t] is True iff key t <= query position pos[j] (masked self-attention)."""
+    return np.arange(n_keys)[None, :] <= np.asarray(pos)[:, None]
+
+
+def prefill(cache, block_table, max_blocks, seq_lens, cu_q_lens, q_nope, q_rope, w_uk, w_uv,
+            rows_sel: Optional[Sequence[int]] = None, heads: Optional[Iterable[int]] = None):
+    """Causal chunked prefill in expanded form, float64.
+
+    Query j of sequence b (cu_q_lens[b] <= j < cu_q_lens[b+1]) sits at position
+    p = L_b - q_len_b + (j - cu_q_lens[b]) and sees keys t <= p ([P3] "大模型的整體推理過程":
+    masked self-attention over the prompt).
+    q_nope [Tq, H, d_nope], q_rope [Tq, H, d_R] rotated at p. Returns out [Tq, H, d_v], lse [Tq, H]
+    (NaN where not selected).
+    """
+    Tq, H, d_nope = q_nope.shape
+    d_r = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    scale = softmax_scale(d_nope, d_r)
+    out = np.full((Tq, H, d_v), np.nan)
+    lse = np.full((Tq, H), np.nan)
+    wk = bf16_to_f64(w_uk)
+    wv = bf16_to_f64(w_uv)
+    hs = _as_list(heads, H)
+    B = len(seq_lens)
+    sel = set(range(Tq)) if rows_sel is None else set(int(r) for r in rows_sel)
+    for b in range(B):
+        q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        js = [j for j in range(q0, q1) if j in sel]
+        if not js:
+            continue
+        L = int(seq_lens[b])
+        qlen = q1 - q0
+        pos = np.array([L - qlen + (j - q0) for j in js], dtype=np.int64)
+        Lmax = int(pos.max()) + 1
+        rows = gather_rows(cache, block_table, max_blocks, b, Lmax)
+        c, kr = rows[:, :d_c], rows[:, d_c:]
+        qn = bf16_to_f64(q_nope[js])                                      # [j, H, d_nope]
+        qr = bf16_to_f64(q_rope[js])
+        mask = causal_visible(pos, Lmax)                                  # [j, t]
+        step = _head_chunk(Lmax, d_nope + d_v + len(js))
+        for i in range(0, len(hs), step):
+            hh = hs[i:i + step]
+            K, V = expand_kv(c, wk[hh], wv[hh])
+            k_full = np.concatenate([K, np.broadcast_to(kr, (len(hh),) + kr.shape)], axis=2)   # [h, t, 192]
+            q_full = np.concatenate([qn[:, hh], qr[:, hh]], axis=2)                            # [j, h, 192]
+            s = np.einsum("jhd,htd->jht", q_full, k_full) * scale
+            s = np.where(mask[:, None, :], s, -np.inf)
+            p, l = softmax_lse(s)
+            o = np.einsum("jht,htd->jhd", p, V)
+            for a, j in enumerate(js):
+                out[j, hh] = o[a]
+                lse[j, hh] = l[a]
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- absorbed form (for the identity check)
+
+def decode_absorbed(cache, block_table, max_blocks, seq_lens, q_nope, q_rope, w_uk, w_uv,
+                    seqs=None, heads=None):
+    """The same decode computed in absorbed form, float64: q_abs = W_UK[h]^T q_nope,
+    s_t = scale (q_abs . c_t + q_R . k_R,t), o_lat = sum_t p_t c_t, out = W_UV[h] o_lat.
+    ([P1] section 4: Q_absorbed = Q W_UK^T scored against c^KV; [P3] "MLA的數學原理".)
+    """
+    B, H, d_nope = q_nope.shape
+    d_r = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    scale = softmax_scale(d_nope, d_r)
+    out = np.full((B, H, d_v), np.nan)
+    lse = np.full((B, H), np.nan)
+    wk = bf16_to_f64(w_uk)
+    wv = bf16_to_f64(w_uv)
+    hs = _as_list(heads, H)
+    for b in _as_list(seqs, B):
+        L = int(seq_lens[b])
+        if L == 0:
+            out[b, hs] = 0.0
+            lse[b, hs] = -np.inf
+            continue
+        rows = gather_rows(cache, block_table, max_blocks, b, L)
+        c, kr = rows[:, :d_c], rows[:, d_c:]
+        q_abs = np.einsum("hdc,hd->hc", wk[hs], bf16_to_f64(q_nope[b, hs]))         # [h, d_c]
+        s = (q_abs @ c.T + bf16_to_f64(q_rope[b, hs]) @ kr.T) * scale               # [h, L]
+        p, l = softmax_lse(s)
+        o_lat = p @ c                                                               # [h, d_c]
+        out[b, hs] = np.einsum("hvc,hc->hv", wv[hs], o_lat)
+        lse[b, hs] = l
+    return out, lse
+
+
+def decode_split_partials(cache, block_table, max_blocks, seq_lens, q_nope, q_rope, w_uk,
+                          split_tokens: int, num_splits: int, seqs=None, heads=None):
+    """Per-split latent partials of absorbed decode: split s covers tokens
+    [s*split_tokens, min((s+1)*split_tokens, L)); o[b,h,s] = softmax-within-split weighted sum of
+    c_t, lse[b,h,s] the split's log-sum-exp (-inf and o = 0 for an empty split).
+    Returns o [B, H, S, d_c], lse [B, H, S].
+    """
+    B, H, d_nope = q_nope.shape
+    d_r = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    scale = softmax_scale(d_nope, d_r)
+    o = np.full((B, H, num_splits, d_c), np.nan)
+    lse = np.full((B, H, num_splits), np.nan)
+    wk = bf16_to_f64(w_uk)
+    hs = _as_list(heads, H)
+    for b in _as_list(seqs, B):
+        L = int(seq_lens[b])
+        rows = gather_rows(cache, block_table, max_blocks, b, L)
+        c, kr = rows[:, :d_c], rows[:, d_c:]
+        q_abs = np.einsum("hdc,hd->hc", wk[hs], bf16_to_f64(q_nope[b, hs]))
+        s_all = (q_abs @ c.T + bf16_to_f64(q_rope[b, hs]) @ kr.T) * scale
+        for s in range(num_splits):
+            t0, t1 = s * split_tokens, min((s + 1) * split_tokens, L)
+            if t1 <= t0:
+                o[b, hs, s] = 0.0
+                lse[b, hs, s] = -np.inf
+                continue
+            p, l = softmax_lse(s_all[:, t0:t1])
+            o[b, hs, s] = p @ c[t0:t1]
+            lse[b, hs, s] = l
+    return o, lse
+
+
+def combine(o_partial: np.ndarray, lse_partial: np.ndarray, w_uv: np.ndarray):
+    """Log-sum-exp merge of split partials, then the W_UV up-projection, float64.
+
+    lse* = log sum_s exp(lse_s); o_lat = sum_s exp(lse_s - lse*) o_s; out[h] = W_UV[h] o_lat.
+    Splits with lse = -inf weigh nothing; if all are -inf the output is 0 and lse* = -inf.
+    o_partial [B, H, S, d_c] float; lse_partial [B, H, S]; w_uv [H, d_v, d_c] bf16.
+    """
+    o_partial = np.asarray(o_partial, dtype=np.float64)
+    lse_partial = np.asarray(lse_partial, dtype=np.float64)
+    m = np.max(lse_partial, axis=2, keepdims=True)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_partial), np.exp(lse_partial - m_safe), 0.0)    # [B, H, S]
+    z = np.sum(w, axis=2, keepdims=True)
+    lse = np.where(finite, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)[..., 0]
+    wn = np.where(finite, w / np.where(z > 0, z, 1.0), 0.0)
+    o_lat = np.einsum("bhs,bhsc->bhc", wn, np.where(wn[..., None] > 0, o_partial, 0.0))
+    out = np.einsum("hvc,bhc->bhv", bf16_to_f64(w_uv), o_lat)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+def cache_elems_per_token(d_c: int, d_rope: int) -> int:
+    """Latent cache per token per layer: d_c + d_R elements ([P1] section 1 formula; [P4] section 一)."""
+    return d_c + d_rope
+
+
+def mha_elems_per_token(n_heads: int, d_head: int) -> int:
+    """Standard MHA cache per token per layer: 2 n_h d_h elements ([P1] section 1; [P4] section 一)."""
+    return 2 * n_heads * d_head
+
+
+def decode_flops_per_token(n_heads: int, d_c: int, d_rope: int) -> int:
+    """Absorbed decode work per cached token: n_h (2 (d_c + d_R) for the score + 2 d_c for p.c)."""
+    return n_heads * (2 * (d_c + d_rope) + 2 * d_c)

@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for weight-absorbed MLA decode and chunked prefill.
+
+This module only draws random numbers, rounds them to bf16 and lays out integer
+tables. It holds none of the attention arithmetic: RoPE, absorption, softmax and
+the cache append are done by each consumer on its own (the fp64 oracle on the
+CPU, the HIP library on the GPU).
+
+Shapes follow the DeepSeek-V2 dimensions quoted on the pages (xuquant.com,
+"Multi-Head Latent Attention: DeepSeek V2/V3 工程视角", section 一: n_h = 128,
+d_c = 4 d_h = 512, d_h^R = d_h / 2 = 64) and the module sketched on
+m.xxqk.cn/news/291060, section 2 (qk_nope_head_dim = 128, qk_rope_head_dim = 64,
+v_head_dim = 128, kv_lora_rank = 512).
+
+Value distributions (the plainest reading of the workload statements):
+  * c_KV, k_R (before rotation), q_nope, q_R (before rotation) ~ N(0, 1);
+  * W_UK, W_UV ~ N(0, std = 1/sqrt(512)), so that the per-head key
+    W_UK[h] c has unit variance and the scaled logits have unit variance;
+  * every value is rounded once, fp64 -> bf16, round-to-nearest-even.
+
+Draw order for one case (numpy PCG64, seed = 20260000 + config index by default):
+  lengths -> c_KV -> k_R -> q_nope -> q_R -> W_UK -> W_UV -> block permutation.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+D_C = 512
+D_ROPE = 64
+D_NOPE = 128
+D_V = 128
+BLOCK = 64
+ROW = D_C + D_ROPE  # elements per cached token
+BF16_NAN = np.uint16(0x7FC0)
+SEED_BASE = 20260000
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (round-to-nearest-even), returned as uint16 bit patterns.
+
+    One direct fp64 -> bf16 rounding (no fp32 intermediate). Values here are finite normals.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0) / 256.0          # 8 significant bits, ties to even
+    y = np.ldexp(q, e).astype(np.float32)   # exact: y has <= 8 significant bits
+    return (y.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Case:
+    """One synthetic workload. All float arrays are bf16 bit patterns (uint16)."""
+    name: str
+    n_heads: int
+    seq_lens: np.ndarray          # [B] int32, cached tokens per sequence after the append
+    q_lens: np.ndarray            # [B] int32, query tokens per sequence (1 for decode)
+    token_seq: np.ndarray         # [T] int32, sequence of every cached token
+    token_pos: np.ndarray         # [T] int32, absolute position of every cached token
+    c_kv: np.ndarray              # [T, 512] uint16
+    k_rope: np.ndarray            # [T, 64] uint16, not yet rotated
+    q_nope: np.ndarray            # [total_q, n_h, 128] uint16
+    q_rope: np.ndarray            # [total_q, n_h, 64] uint16, not yet rotated
+    w_uk: np.ndarray              # [n_h, 128, 512] uint16
+    w_uv: np.ndarray              # [n_h, 128, 512] uint16
+    num_blocks: int               # physical blocks in the pool
+    block_table: Optional[np.ndarray]  # [B, max_blocks] int32, or None for the contiguous layout
+    max_blocks_per_seq: int
+    prefill: bool
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def cu_q_lens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+
+    @property
+    def cu_tokens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int64)
+
+    def q_positions(self) -> np.ndarray:
+        """Absolute position of every query token: the last q_len positions of its sequence."""
+        out = []
+        for b in range(self.batch):
+            L, q = int(self.seq_lens[b]), int(self.q_lens[b])
+            out.append(np.arange(L - q, L, dtype=np.int32))
+        return np.concatenate(out) if out else np.zeros(0, np.int32)
+
+    def q_seq(self) -> np.ndarray:
+        return np.repeat(np.arange(self.batch, dtype=np.int32), self.q_lens)
+
+    def physical_block(self, b: int, i: int) -> int:
+        if self.block_table is None:
+            return b * self.max_blocks_per_seq + i
+        return int(self.block_table[b, i])
+
+    def new_token_index(self) -> np.ndarray:
+        """Indices (into the token arrays) of the tokens a step appends: the last q_len of each sequence."""
+        cu = self.cu_tokens
+        idx = []
+        for b in range(self.batch):
+            q = int(self.q_lens[b])
+            idx.append(np.arange(cu[b + 1] - q, cu[b + 1], dtype=np.int64))
+        return np.concatenate(idx) if idx else np.zeros(0, np.int64)
+
+
+def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) draws rounded to bf16, drawn in row chunks to bound host memory.
+
+    Chunked draws consume the generator's stream in the same order as one large draw.
+    """
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, np.uint16)
+    if out.size == 0:
+        return out
+    rows = shape[0]
+    per_row = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    step = max(1, (1 << 24) // max(per_row, 1))
+    flat = out.reshape(rows, per_row)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        flat[r0:r1] = bf16_bits(rng.standard_normal(size=(r1 - r0, per_row)) * std)
+    return out
+
+
+def make_case(name: str, seed: int, n_heads: int, seq_lens: Sequence[int], q_lens: Optional[Sequence[int]] = None,
+              paged: bool = False, spare_blocks: int = 0, rand_lens: Optional[tuple] = None,
+              batch: Optional[int] = None) -> Case:
+    """Draw one case.
+
+    seq_lens: cached tokens per sequence (decode: including the token being appended).
+    q_lens: query tokens per sequence (default 1 each: decode).
+    paged: shuffled block table over a pool of sum(ceil(L/64)) + spare_blocks blocks;
+           otherwise the contiguous layout (block i of sequence b is physical b*max_blocks+i).
+    rand_lens: (lo, hi, batch) -> lengths drawn uniform in [lo, hi] inclusive (first draw).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if rand_lens is not None:
+        lo, hi, nb = rand_lens
+        seq_lens = rng.integers(lo, hi + 1, size=nb)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = seq_lens.shape[0]
+    q_lens = np.ones(B, np.int32) if q_lens is None else np.asarray(q_lens, np.int32)
+    assert q_lens.shape == (B,) and np.all(q_lens <= np.maximum(seq_lens, 0))
+    T = int(seq_lens.sum())
+    c_kv = _normal_bf16(rng, (T, D_C))
+    k_rope = _normal_bf16(rng, (T, D_ROPE))
+    tq = int(q_lens.sum())
+    q_nope = _normal_bf16(rng, (tq, n_heads, D_NOPE))
+    q_rope = _normal_bf16(rng, (tq, n_heads, D_ROPE))
+    w_std = 1.0 / math.sqrt(D_C)
+    w_uk = _normal_bf16(rng, (n_heads, D_NOPE, D_C), w_std)
+    w_uv = _normal_bf16(rng, (n_heads, D_V, D_C), w_std)
+    nblk = [(int(L) + BLOCK - 1) // BLOCK for L in seq_lens]
+    max_blocks = max(1, max(nblk) if nblk else 1)
+    if paged:
+        used = int(sum(nblk))
+        num_blocks = used + spare_blocks
+        perm = rng.permutation(num_blocks).astype(np.int32)
+        table = np.empty((B, max_blocks), np.int32)
+        k = 0
+        spare = perm[used:] if spare_blocks > 0 else None
+        for b in range(B):
+            table[b, :nblk[b]] = perm[k:k + nblk[b]]
+            k += nblk[b]
+            # entries past the sequence's last block point at a spare (poisoned) block if there is one
+            table[b, nblk[b]:] = spare[b % len(spare)] if spare is not None else 0
+    else:
+        table = None
+        num_blocks = B * max_blocks
+    token_seq = np.repeat(np.arange(B, dtype=np.int32), seq_lens)
+    token_pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in seq_lens]) if T else np.zeros(0, np.int32)
+    return Case(name=name, n_heads=n_heads, seq_lens=seq_lens, q_lens=q_lens, token_seq=token_seq,
+                token_pos=token_pos, c_kv=c_kv, k_rope=k_rope, q_nope=q_nope, q_rope=q_rope, w_uk=w_uk,
+                w_uv=w_uv, num_blocks=num_blocks, block_table=table, max_blocks_per_seq=max_blocks,
+                prefill=bool(np.any(q_lens > 1)))
+
+
+CONFIG_NAMES = [
+    "tiny decode B=1 n_h=16 L=256",
+    "decode B=32 n_h=128 L=4096 contiguous",
+    "ragged paged decode B=64 n_h=128 L~U[512,32768] 64-token blocks",
+    "long split-KV decode B=4 n_h=128 L=131072",
+    "chunked prefill B=2 n_h=128 1024 new after 8192, causal",
+]
+
+
+def make_config(i: int, seed: Optional[int] = None) -> Case:
+    """The five workloads: tiny decode, the 4K decode, ragged paged decode, 128K decode, chunked prefill."""
+    s = SEED_BASE + i if seed is None else seed
+    if i == 0:
+        return make_case(CONFIG_NAMES[0], s, 16, [256])
+    if i == 1:
+        return make_case(CONFIG_NAMES[1], s, 128, [4096] * 32)
+    if i == 2:
+        return make_case(CONFIG_NAMES[2], s, 128, [], paged=True, spare_blocks=64, rand_lens=(512, 32768, 64))
+    if i == 3:
+        return make_case(CONFIG_NAMES[3], s, 128, [131072] * 4)
+    if i == 4:
+        return make_case(CONFIG_NAMES[4], s, 128, [8192 + 1024] * 2, q_lens=[1024] * 2)
+    raise ValueError(f"no config {i}")
