@@ -1,0 +1,167 @@
+// C ABI of the MLA library: host-side validation, workspace layout and kernel launches.
+// Every check happens before the first HIP call, so an invalid call enqueues nothing.
+#include <math.h>
+#include <stddef.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->n_heads <= 0 || d->d_c <= 0 || d->d_rope <= 0 || d->d_nope <= 0 || d->d_v <= 0 || d->block_size <= 0)
+    return MLA_ERR_BAD_ARG;
+  if (!(d->scale > 0.f) || !isfinite(d->scale)) return MLA_ERR_BAD_ARG;
+  if (!(d->rope_theta > 1.f) || !isfinite(d->rope_theta)) return MLA_ERR_BAD_ARG;
+  if (d->d_c != mla::kDc || d->d_rope != mla::kDr || d->d_nope != mla::kDnope || d->d_v != mla::kDv ||
+      d->block_size != mla::kBlock || d->n_heads % 16 != 0 || d->n_heads > 65535)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int check_cache(const mla_cache* c) {
+  if (!c || !c->data) return MLA_ERR_NULL;
+  if (c->num_blocks <= 0 || c->max_blocks_per_seq <= 0) return MLA_ERR_BAD_ARG;
+  return MLA_OK;
+}
+
+mla::CacheView view(const mla_cache* c) { return mla::CacheView{c->data, c->block_table, c->max_blocks_per_seq}; }
+
+int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+struct PrefillWorkspace {
+  size_t q_abs, o_lat, lse, total;
+};
+
+PrefillWorkspace prefill_layout(const mla_dims* d, int32_t total_q) {
+  PrefillWorkspace w;
+  size_t rows = (size_t)(total_q > 0 ? total_q : 0) * (size_t)d->n_heads;
+  w.q_abs = 0;
+  w.o_lat = align256(rows * mla::kRow * 2);
+  w.lse = w.o_lat + align256(rows * mla::kDc * 4);
+  w.total = w.lse + align256(rows * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_BAD_ARG: return "MLA_ERR_BAD_ARG: a size is out of range or inconsistent";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this shape";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: the HIP runtime rejected a launch";
+    default: return "unknown MLA status";
+  }
+}
+
+int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens, const int32_t* token_seq,
+                    const int32_t* token_pos, const uint16_t* c_kv, const uint16_t* k_rope, uint16_t* q_rope_inout,
+                    hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (num_tokens < 0) return MLA_ERR_BAD_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!token_seq || !token_pos || !c_kv || !k_rope) return MLA_ERR_NULL;
+  return launched(mla::launch_rope_append(view(cache), dims->n_heads, num_tokens, token_seq, token_pos, c_kv, k_rope,
+                                          q_rope_inout, dims->rope_theta, stream));
+}
+
+int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, int32_t num_cus,
+                    int32_t* split_tokens, int32_t* num_splits) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!split_tokens || !num_splits) return MLA_ERR_NULL;
+  if (batch <= 0 || max_seq_len < 0 || num_cus <= 0) return MLA_ERR_BAD_ARG;
+  const int64_t bs = dims->block_size;
+  const int64_t blocks = (max_seq_len + bs - 1) / bs;
+  // enough splits per sequence that batch * splits covers every compute unit once
+  int64_t per_seq = (num_cus + batch - 1) / batch;
+  if (per_seq < 1) per_seq = 1;
+  if (blocks > 0 && per_seq > blocks) per_seq = blocks;
+  int64_t blocks_per_split = blocks > 0 ? (blocks + per_seq - 1) / per_seq : 1;
+  int64_t tok = blocks_per_split * bs;
+  int64_t ns = blocks > 0 ? (blocks + blocks_per_split - 1) / blocks_per_split : 1;
+  if (tok > INT32_MAX || ns > 65535) return MLA_ERR_BAD_ARG;
+  *split_tokens = (int32_t)tok;
+  *num_splits = (int32_t)ns;
+  return MLA_OK;
+}
+
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch) {
+  if (check_dims(dims) != MLA_OK || batch < 0) return 0;
+  return align256((size_t)batch * dims->n_heads * mla::kRow * 2);
+}
+
+int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+               const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int32_t split_tokens,
+               int32_t num_splits, void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial,
+               hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0 || batch > 65535) return MLA_ERR_BAD_ARG;
+  if (split_tokens <= 0 || split_tokens % dims->block_size != 0) return MLA_ERR_BAD_ARG;
+  if (num_splits <= 0 || num_splits > 65535) return MLA_ERR_BAD_ARG;
+  if ((int64_t)split_tokens * num_splits > (int64_t)INT32_MAX) return MLA_ERR_BAD_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!seq_lens || !q_nope || !q_rope || !w_uk || !workspace || !o_partial || !lse_partial) return MLA_ERR_NULL;
+  if (workspace_bytes < mla_decode_workspace_size(dims, batch)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  uint16_t* q_abs = static_cast<uint16_t*>(workspace);
+  hipError_t e = mla::launch_absorb(batch, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  return launched(mla::launch_decode_attention(view(cache), batch, dims->n_heads, seq_lens, q_abs, dims->scale,
+                                               split_tokens, num_splits, o_partial, lse_partial, stream));
+}
+
+int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const float* o_partial,
+                       const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
+                       hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || num_splits <= 0 || num_splits > 65535) return MLA_ERR_BAD_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!o_partial || !lse_partial || !w_uv || !out) return MLA_ERR_NULL;
+  return launched(mla::launch_combine(batch, dims->n_heads, num_splits, o_partial, lse_partial, w_uv, out, lse_out,
+                                      stream));
+}
+
+size_t mla_chunked_prefill_workspace_size(const mla_dims* dims, int32_t total_q) {
+  if (check_dims(dims) != MLA_OK || total_q < 0) return 0;
+  return prefill_layout(dims, total_q).total;
+}
+
+int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                        const int32_t* cu_q_lens, int32_t total_q, int32_t max_q_len, const uint16_t* q_nope,
+                        const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv, void* workspace,
+                        size_t workspace_bytes, uint16_t* out, float* lse_out, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || total_q > 65535) return MLA_ERR_BAD_ARG;
+  if (batch == 0 || total_q == 0) return MLA_OK;
+  if (!seq_lens || !cu_q_lens || !q_nope || !q_rope || !w_uk || !w_uv || !workspace || !out) return MLA_ERR_NULL;
+  PrefillWorkspace lay = prefill_layout(dims, total_q);
+  if (workspace_bytes < lay.total) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + lay.q_abs);
+  float* o_lat = reinterpret_cast<float*>(ws + lay.o_lat);
+  float* lse = reinterpret_cast<float*>(ws + lay.lse);
+  hipError_t e = mla::launch_absorb(total_q, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  e = mla::launch_prefill_attention(view(cache), batch, dims->n_heads, seq_lens, cu_q_lens, total_q, max_q_len, q_abs,
+                                    dims->scale, o_lat, lse, stream);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  return launched(mla::launch_combine(total_q, dims->n_heads, 1, o_lat, lse, w_uv, out, lse_out, stream));
+}
+
+}  // extern "C"

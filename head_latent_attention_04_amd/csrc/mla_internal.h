@@ -1,0 +1,75 @@
+// Internal declarations shared by the kernels and the C-ABI layer of the MLA library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// The one shape the kernels are written for (DeepSeek-V2 dimensions: "Multi-Head Latent Attention:
+// DeepSeek V2/V3 工程视角", section 一; module defaults of "论文复现工坊 No.4", section 2).
+constexpr int kDc = 512;            // latent c_KV width
+constexpr int kDr = 64;             // decoupled RoPE width
+constexpr int kRow = kDc + kDr;     // 576 elements per cached token
+constexpr int kRowBytes = kRow * 2; // 1152 bytes in bf16
+constexpr int kDnope = 128;
+constexpr int kDv = 128;
+constexpr int kBlock = 64;          // tokens per cache block
+
+struct CacheView {
+  uint16_t* data;
+  const int32_t* table;  // nullptr: contiguous
+  int32_t max_blocks;
+};
+
+// ---- bf16 helpers -------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// double -> bf16, round to nearest even: first to float rounding toward zero with a sticky
+// low bit (round-to-odd), which keeps the exact tie information, then float -> bf16 RNE.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  float t = __double2float_rz(x);
+  uint32_t u = __float_as_uint(t);
+  if ((double)t != x) u |= 1u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ int64_t row_offset(const CacheView& c, int seq, int pos) {
+  int blk = pos / kBlock;
+  int64_t phys = c.table ? (int64_t)c.table[(int64_t)seq * c.max_blocks + blk]
+                         : (int64_t)seq * c.max_blocks + blk;
+  return (phys * kBlock + (pos % kBlock)) * (int64_t)kRow;
+}
+
+// ---- launchers (each returns the launch status) ---------------------------------------------------
+hipError_t launch_rope_append(const CacheView& cache, int n_heads, int num_tokens, const int32_t* token_seq,
+                              const int32_t* token_pos, const uint16_t* c_kv, const uint16_t* k_rope,
+                              uint16_t* q_rope, float theta, hipStream_t stream);
+
+// q_abs[r, h, 0:512] = W_UK[h]^T q_nope[r, h]; q_abs[r, h, 512:576] = q_rope[r, h] (bf16), r < rows.
+hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
+                         const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream);
+
+// Split-KV decode attention over the latent cache (rows = heads of one query token).
+hipError_t launch_decode_attention(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
+                                   const uint16_t* q_abs, float scale, int split_tokens, int num_splits,
+                                   float* o_partial, float* lse_partial, hipStream_t stream);
+
+// Causal prefill attention producing normalised latent outputs and lse per (query, head).
+hipError_t launch_prefill_attention(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
+                                    const int32_t* cu_q_lens, int total_q, int max_q_len, const uint16_t* q_abs,
+                                    float scale, float* o_lat, float* lse, hipStream_t stream);
+
+// LSE merge over splits + W_UV up-projection.
+hipError_t launch_combine(int batch, int n_heads, int num_splits, const float* o_partial, const float* lse_partial,
+                          const uint16_t* w_uv, uint16_t* out, float* lse_out, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,187 @@
+"""Thin ctypes binding of libmla.so (the C ABI in include/mla.h).
+
+Argument marshalling only: tensors are passed as device pointers, shapes are checked
+against the C contract, and the current torch stream is handed over. Every step of the
+computation runs in the HIP kernels of libmla.so. If the library has not been built, the
+first call raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+D_C, D_ROPE, D_NOPE, D_V, BLOCK = 512, 64, 128, 128, 64
+ROW = D_C + D_ROPE
+
+MLA_OK, MLA_ERR_NULL, MLA_ERR_BAD_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH = 0, -1, -2, -3, -4
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("n_heads", _i32), ("d_c", _i32), ("d_rope", _i32), ("d_nope", _i32), ("d_v", _i32),
+                ("block_size", _i32), ("scale", _f32), ("rope_theta", _f32)]
+
+
+class MlaCache(ctypes.Structure):
+    _fields_ = [("data", _vp), ("num_blocks", _i64), ("block_table", _vp), ("max_blocks_per_seq", _i32)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text} ({status})")
+        self.status = status
+
+
+EXPORTS = {
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_rope_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp,
+                                       _vp, _vp]),
+    "mla_decode_plan": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                       ctypes.POINTER(_i32)]),
+    "mla_decode_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
+    "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp, _i32,
+                                  _i32, _vp, _sz, _vp, _vp, _vp]),
+    "mla_decode_combine": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_chunked_prefill_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
+    "mla_chunked_prefill": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
+                                           _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (once). Raises if it is missing: there is no other implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing; build it with `python -m head_latent_attention_04_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MLA_OK:
+        raise MLAError(fn, status, status_string(status))
+
+
+def make_dims(n_heads: int, scale: Optional[float] = None, rope_theta: float = 10000.0, d_c: int = D_C,
+              d_rope: int = D_ROPE, d_nope: int = D_NOPE, d_v: int = D_V, block_size: int = BLOCK) -> MlaDims:
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_nope + d_rope)
+    return MlaDims(n_heads, d_c, d_rope, d_nope, d_v, block_size, scale, rope_theta)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None, numel: Optional[int] = None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+I32 = (torch.int32,)
+F32 = (torch.float32,)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_cache(data: torch.Tensor, block_table: Optional[torch.Tensor], max_blocks_per_seq: int) -> MlaCache:
+    """data: [num_blocks, 64, 576] bf16 (or its int16 view); block_table: [batch, max_blocks] int32 or None."""
+    if data.dim() != 3 or data.shape[1] != BLOCK or data.shape[2] != ROW:
+        raise ValueError("cache data must be [num_blocks, 64, 576]")
+    return MlaCache(_ptr(data, "cache", BF16), data.shape[0], _ptr(block_table, "block_table", I32),
+                    max_blocks_per_seq)
+
+
+def rope_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_rope, q_rope=None, stream=None):
+    T = token_seq.numel()
+    st = load().mla_rope_append(
+        ctypes.byref(dims), ctypes.byref(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        _ptr(token_pos, "token_pos", I32, T), _ptr(c_kv, "c_kv", BF16, T * dims.d_c),
+        _ptr(k_rope, "k_rope", BF16, T * dims.d_rope),
+        _ptr(q_rope, "q_rope", BF16, T * dims.n_heads * dims.d_rope), _stream(stream))
+    _check("mla_rope_append", st)
+
+
+def decode_plan(dims: MlaDims, batch: int, max_seq_len: int, num_cus: int) -> Tuple[int, int]:
+    a, b = _i32(), _i32()
+    _check("mla_decode_plan", load().mla_decode_plan(ctypes.byref(dims), batch, max_seq_len, num_cus,
+                                                     ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def decode_workspace_size(dims: MlaDims, batch: int) -> int:
+    return int(load().mla_decode_workspace_size(ctypes.byref(dims), batch))
+
+
+def decode(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split_tokens: int, num_splits: int,
+           workspace, o_partial, lse_partial, stream=None):
+    B = seq_lens.numel()
+    H = dims.n_heads
+    st = load().mla_decode(
+        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(q_nope, "q_nope", BF16, B * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, B * H * dims.d_rope),
+        _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), split_tokens, num_splits,
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(o_partial, "o_partial", F32, B * H * num_splits * dims.d_c),
+        _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
+    _check("mla_decode", st)
+
+
+def decode_combine(dims: MlaDims, batch: int, num_splits: int, o_partial, lse_partial, w_uv, out, lse_out=None,
+                   stream=None):
+    H = dims.n_heads
+    st = load().mla_decode_combine(
+        ctypes.byref(dims), batch, num_splits, _ptr(o_partial, "o_partial", F32, batch * H * num_splits * dims.d_c),
+        _ptr(lse_partial, "lse_partial", F32, batch * H * num_splits),
+        _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c), _ptr(out, "out", BF16, batch * H * dims.d_v),
+        _ptr(lse_out, "lse_out", F32, batch * H), _stream(stream))
+    _check("mla_decode_combine", st)
+
+
+def chunked_prefill_workspace_size(dims: MlaDims, total_q: int) -> int:
+    return int(load().mla_chunked_prefill_workspace_size(ctypes.byref(dims), total_q))
+
+
+def chunked_prefill(dims: MlaDims, cache: MlaCache, seq_lens, cu_q_lens, max_q_len: int, q_nope, q_rope, w_uk, w_uv,
+                    workspace, out, lse_out=None, stream=None):
+    B = seq_lens.numel()
+    H = dims.n_heads
+    Tq = q_nope.shape[0]
+    st = load().mla_chunked_prefill(
+        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(cu_q_lens, "cu_q_lens", I32, B + 1), Tq, max_q_len,
+        _ptr(q_nope, "q_nope", BF16, Tq * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, Tq * H * dims.d_rope),
+        _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out", BF16, Tq * H * dims.d_v), _ptr(lse_out, "lse_out", F32, Tq * H), _stream(stream))
+    _check("mla_chunked_prefill", st)

@@ -1,0 +1,177 @@
+/*
+ * mla.h - C ABI of the weight-absorbed Multi-Head Latent Attention (MLA) library for gfx950.
+ *
+ * The library computes MLA decode and chunked prefill over a paged, compressed latent KV
+ * cache in which each token keeps one row [c_KV (d_c) | k_R (d_rope)] shared by all heads.
+ * Per head, q_nope is absorbed through W_UK into the latent space, scored against the row
+ * together with the decoupled-RoPE query, the softmax weights reduce c_KV, and the reduced
+ * latent is up-projected through W_UV.
+ *
+ * Sources (page title, section):
+ *   "论文复现工坊 No.4：从零复现 DeepSeek-V2/V3 多头潜在注意力 MLA" (m.xxqk.cn), sections 1, 2, 4:
+ *       latent c_KV cached with a decoupled RoPE key; the module's shapes and its scale
+ *       1/sqrt(qk_nope_head_dim + qk_rope_head_dim); Q_absorbed = Q W_UK^T scored against c^KV.
+ *   "淺析DeepSeek多頭潛在注意力機制（MLA）" (itdecent.cn), "大模型的整體推理過程",
+ *       "MLA的數學原理", "MLA與ROPE的融合": decode appends the new token then attends over
+ *       all cached tokens; x_t (W_q W_k^T) c_i^T; RoPE angle theta_i = 10000^(-2i/d) and a
+ *       RoPE key shared by all heads.
+ *   "Multi-Head Latent Attention: DeepSeek V2/V3 工程视角" (xuquant.com), section 一:
+ *       n_h = 128, d_c = 512, d_h^R = 64, 576 cached elements per token per layer.
+ *   "Multi-Head Latent Attention（MLA）原理与工程实践全解析" (cnnetsun.cn), section 3.3:
+ *       flattened [batch, seq, latent] cache rows and block-managed (paged) storage.
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is a DEVICE pointer; bf16 values are passed as uint16_t bit patterns;
+ *     all integer tables are int32. The caller owns every buffer; the library allocates nothing,
+ *     keeps no state between calls and never synchronises.
+ *   - Work is enqueued on `stream` and runs asynchronously. Calls are safe to capture in a graph.
+ *   - Arguments are validated on the host before any HIP call. A call returns MLA_OK (0) or a
+ *     negative status; on an error nothing has been enqueued (except MLA_ERR_LAUNCH, reported
+ *     after a launch failed).
+ *   - Contents of device buffers are a caller contract that the host cannot check: block ids
+ *     must lie in [0, num_blocks), every seq_len must satisfy
+ *     0 <= seq_len <= max_blocks_per_seq * block_size, positions must be < seq_len.
+ *   - Supported shapes: d_c = 512, d_rope = 64, d_nope = 128, d_v = 128, block_size = 64,
+ *     n_heads a positive multiple of 16. Others return MLA_ERR_UNSUPPORTED.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MLA_ERR_BAD_ARG (-2)     /* a size is negative, zero where it must be positive, or inconsistent */
+#define MLA_ERR_UNSUPPORTED (-3) /* a shape this library has no kernel for */
+#define MLA_ERR_LAUNCH (-4)      /* the HIP runtime reported an error for a launch */
+
+/* Model dimensions ("论文复现工坊 No.4", section 2: the module's constructor arguments). */
+typedef struct mla_dims {
+  int32_t n_heads;    /* query heads n_h; multiple of 16 */
+  int32_t d_c;        /* latent width (kv_lora_rank), 512 */
+  int32_t d_rope;     /* decoupled RoPE width (qk_rope_head_dim), 64 */
+  int32_t d_nope;     /* per-head non-RoPE query/key width (qk_nope_head_dim), 128 */
+  int32_t d_v;        /* per-head value width (v_head_dim), 128 */
+  int32_t block_size; /* tokens per cache block, 64 */
+  float scale;        /* softmax scale, normally 1/sqrt(d_nope + d_rope); must be finite and > 0 */
+  float rope_theta;   /* RoPE base, normally 10000; must be > 1 */
+} mla_dims;
+
+/* Paged latent cache. Row of token t of sequence b lives at
+ *   data + ((int64)phys * block_size + t % block_size) * (d_c + d_rope),
+ *   phys = block_table[b * max_blocks_per_seq + t / block_size]   (paged), or
+ *   phys = b * max_blocks_per_seq + t / block_size                 (block_table == NULL: contiguous).
+ * A row is [c_KV (d_c) | k_R rotated at t (d_rope)], bf16, 1152 bytes at the supported shape. */
+typedef struct mla_cache {
+  uint16_t* data;             /* [num_blocks, block_size, d_c + d_rope] bf16 */
+  int64_t num_blocks;         /* > 0 */
+  const int32_t* block_table; /* [batch, max_blocks_per_seq] int32, or NULL */
+  int32_t max_blocks_per_seq; /* > 0 */
+} mla_cache;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mla_status_string(int status);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_rope_append - rotate the decoupled RoPE key and query of new tokens and append the keys.
+ * ("淺析DeepSeek多頭潛在注意力機制（MLA）", "MLA與ROPE的融合"; "论文复现工坊 No.4", sections 1-2.)
+ *
+ * For each new token i (0 <= i < num_tokens) of sequence token_seq[i] at position p = token_pos[i]:
+ *   row = [c_kv[i] | R_p k_rope[i]] is written to the cache slot of (token_seq[i], p);
+ *   if q_rope_inout != NULL, q_rope_inout[i, h, :] = R_p q_rope_inout[i, h, :] for every head h.
+ * R_p turns each interleaved pair (x_{2j}, x_{2j+1}) by p * rope_theta^(-2j/d_rope), computed in
+ * fp64 and rounded to bf16 (round-to-nearest-even).
+ *   c_kv         [num_tokens, d_c] bf16, k_rope [num_tokens, d_rope] bf16 (not rotated)
+ *   token_seq    [num_tokens] int32 in [0, batch of the table)
+ *   token_pos    [num_tokens] int32 >= 0
+ *   q_rope_inout [num_tokens, n_heads, d_rope] bf16, rotated in place (may be NULL)
+ * Two new tokens must not map to the same slot. num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens,
+                    const int32_t* token_seq, const int32_t* token_pos, const uint16_t* c_kv,
+                    const uint16_t* k_rope, uint16_t* q_rope_inout, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Split planning for decode (host only, no HIP call).
+ * Chooses split_tokens (a multiple of block_size) and num_splits = ceil(max_seq_len / split_tokens)
+ * so that batch * num_splits work-groups fill `num_cus` compute units. Returns MLA_OK or an error.
+ * ------------------------------------------------------------------------------------------- */
+int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, int32_t num_cus,
+                    int32_t* split_tokens, int32_t* num_splits);
+
+/* Bytes of device workspace mla_decode needs for `batch` sequences (the absorbed queries). */
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_decode - absorbed decode attention, split over the key axis (one query token per sequence).
+ * ("论文复现工坊 No.4", sections 2 and 4; "淺析DeepSeek多頭潛在注意力機制（MLA）", "MLA的數學原理",
+ *  "大模型的整體推理過程": the query is the sequence's last token and sees all seq_len tokens.)
+ *
+ * For sequence b with L = seq_lens[b] cached tokens, every head h and split s (tokens
+ * [s*split_tokens, min((s+1)*split_tokens, L))):
+ *   q_abs[h]    = W_UK[h]^T q_nope[b, h]                   (d_c, rounded to bf16)
+ *   s_t         = scale * (q_abs[h] . c_t + q_rope[b, h] . kR_t)
+ *   lse_partial[b, h, s] = ln sum_t exp(s_t)                (-inf for an empty split)
+ *   o_partial[b, h, s, :] = sum_t exp(s_t - lse_partial) c_t  (0 for an empty split)
+ *   seq_lens     [batch] int32, 0 <= L <= num_splits * split_tokens
+ *   q_nope       [batch, n_heads, d_nope] bf16
+ *   q_rope       [batch, n_heads, d_rope] bf16, already rotated at position L-1
+ *   w_uk         [n_heads, d_nope, d_c] bf16 (row d of head h maps c to the key's element d)
+ *   split_tokens multiple of block_size, > 0; num_splits > 0
+ *   workspace    >= mla_decode_workspace_size(dims, batch) bytes, 256-byte aligned
+ *   o_partial    [batch, n_heads, num_splits, d_c] fp32
+ *   lse_partial  [batch, n_heads, num_splits] fp32
+ * ------------------------------------------------------------------------------------------- */
+int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+               const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
+               int32_t split_tokens, int32_t num_splits, void* workspace, size_t workspace_bytes,
+               float* o_partial, float* lse_partial, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_decode_combine - log-sum-exp merge of the split partials and the W_UV up-projection.
+ * ("论文复现工坊 No.4", section 1: no K or V tensor is ever expanded; the value side is
+ *  W_UV applied after the latent reduction.)
+ *   lse[b,h]   = ln sum_s exp(lse_partial[b,h,s])        (-inf if every split is empty)
+ *   o_lat      = sum_s exp(lse_partial[b,h,s] - lse[b,h]) o_partial[b,h,s,:]   (fp32)
+ *   out[b,h,:] = W_UV[h] o_lat                             (bf16; 0 if every split is empty)
+ *   w_uv    [n_heads, d_v, d_c] bf16;  out [batch, n_heads, d_v] bf16
+ *   lse_out [batch, n_heads] fp32, natural log (may be NULL)
+ * ------------------------------------------------------------------------------------------- */
+int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const float* o_partial,
+                       const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
+                       hipStream_t stream);
+
+/* Bytes of device workspace mla_chunked_prefill needs for `total_q` query tokens. */
+size_t mla_chunked_prefill_workspace_size(const mla_dims* dims, int32_t total_q);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_chunked_prefill - causal attention of a chunk of new tokens, absorbed form.
+ * ("淺析DeepSeek多頭潛在注意力機制（MLA）", "大模型的整體推理過程": masked self-attention over
+ *  the prompt; the same absorbed scores and latent reduction as decode.)
+ * Query j of sequence b (cu_q_lens[b] <= j < cu_q_lens[b+1]) sits at position
+ *   p = seq_lens[b] - (cu_q_lens[b+1] - cu_q_lens[b]) + (j - cu_q_lens[b])
+ * and attends to cached tokens 0..p (the chunk must already be appended):
+ *   out[j, h, :] = W_UV[h] sum_{t<=p} softmax_t(scale (q_abs . c_t + q_rope[j,h] . kR_t)) c_t
+ *   seq_lens  [batch] int32 (tokens cached, chunk included); cu_q_lens [batch+1] int32, cu_q_lens[0] = 0,
+ *             cu_q_lens[batch] = total_q, each chunk length <= max_q_len and <= its seq_len
+ *   q_nope    [total_q, n_heads, d_nope] bf16;  q_rope [total_q, n_heads, d_rope] bf16 rotated at p
+ *   w_uk, w_uv as for decode;  out [total_q, n_heads, d_v] bf16;  lse_out [total_q, n_heads] fp32 or NULL
+ *   workspace >= mla_chunked_prefill_workspace_size(dims, total_q) bytes, 256-byte aligned
+ * ------------------------------------------------------------------------------------------- */
+int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t batch,
+                        const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t total_q,
+                        int32_t max_q_len, const uint16_t* q_nope, const uint16_t* q_rope,
+                        const uint16_t* w_uk, const uint16_t* w_uv, void* workspace,
+                        size_t workspace_bytes, uint16_t* out, float* lse_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

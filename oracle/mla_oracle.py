@@ -137,10 +137,19 @@ def rope_append(cache: np.ndarray, block_table, max_blocks: int, token_seq, toke
     token_seq = np.asarray(token_seq)
     token_pos = np.asarray(token_pos)
     k_rot = f64_to_bf16(rope_rotate(bf16_to_f64(k_rope), token_pos, theta))
-    for t in range(token_seq.shape[0]):
-        phys, r = slot_of(block_table, max_blocks, bs, int(token_seq[t]), int(token_pos[t]))
-        cache[phys, r, :d_c] = c_kv[t]
-        cache[phys, r, d_c:] = k_rot[t]
+    if token_seq.shape[0] <= 4096:
+        for t in range(token_seq.shape[0]):
+            phys, r = slot_of(block_table, max_blocks, bs, int(token_seq[t]), int(token_pos[t]))
+            cache[phys, r, :d_c] = c_kv[t]
+            cache[phys, r, d_c:] = k_rot[t]
+    else:
+        # the same placement for many tokens at once
+        blk = token_pos.astype(np.int64) // bs
+        phys = (token_seq.astype(np.int64) * max_blocks + blk if block_table is None
+                else np.asarray(block_table)[token_seq, blk].astype(np.int64))
+        r = token_pos.astype(np.int64) % bs
+        cache[phys, r, :d_c] = c_kv
+        cache[phys, r, d_c:] = k_rot
     q_rot = None
     if q_rope is not None:
         q_rot = f64_to_bf16(rope_rotate(bf16_to_f64(q_rope), np.asarray(token_pos)[:, None], theta))

@@ -288,6 +288,22 @@ def pin_slot_mapping():
                 assert np.array_equal(cache[blk, r], cache0[blk, r])
     # contiguous layout: logical block i of sequence b is physical b * maxb + i
     assert O.slot_of(None, 5, 64, 2, 130) == (2 * 5 + 2, 2)
+    # many tokens at once (the batched placement path) against the same dict placement
+    B, maxb, bs = 5, 30, 64
+    lens = [1900, 64, 1, 1111, 1920]
+    nb = B * maxb + 7
+    table = rng.permutation(nb)[:B * maxb].reshape(B, maxb).astype(np.int32)
+    tseq = np.concatenate([np.full(L, b) for b, L in enumerate(lens)]).astype(np.int32)
+    tpos = np.concatenate([np.arange(L) for L in lens]).astype(np.int32)
+    assert len(tseq) > 4096
+    c = rng.integers(0, 1 << 15, size=(len(tseq), 4), dtype=np.uint16)
+    kr = bf16_bits(rng.standard_normal((len(tseq), 2)))
+    cache0 = np.zeros((nb, bs, 6), np.uint16)
+    cache, _ = O.rope_append(cache0, table, maxb, tseq, tpos, c, kr)
+    for i in range(0, len(tseq), 97):
+        b, p = int(tseq[i]), int(tpos[i])
+        assert np.array_equal(cache[int(table[b][p // bs]), p % bs, :4], c[i])
+    assert int((cache[..., :4] != 0).any(axis=2).sum()) == int(((c != 0).any(axis=1)).sum())
 
 
 def pin_closed_forms():
