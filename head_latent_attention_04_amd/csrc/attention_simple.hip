@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(64) prefill_simple_kernel(CacheView cache, int
   if (lane == 0) lse[r] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_decode_attention(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
+hipError_t launch_decode_attention_simple(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
                                    const uint16_t* q_abs, float scale, int split_tokens, int num_splits,
                                    float* o_partial, float* lse_partial, hipStream_t stream) {
   if (batch == 0) return hipSuccess;

@@ -223,3 +223,29 @@ def test_decode_configs_full_size_sampled(cfg):
     sel = np.ix_(seqs, heads)
     assert_close(out[sel], ref[sel], f"config {cfg} sampled")
     assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
+
+
+def test_decode_large_score_growth_uses_exact_path():
+    """Scores that climb by far more than 2^64 after the first sub-tile (q_nope = 0 and the RoPE keys
+    of tokens >= 64 scaled by 64, all exact in bf16): the decode still matches the oracle."""
+    say("[decode] large score growth")
+    case = make_case("growth", 71, 32, [700, 130], paged=True, spare_blocks=2)
+    case.q_nope[:] = 0
+    big = case.token_pos >= 64
+    kr = case.k_rope.astype(np.uint32)
+    exp_field = (kr >> 7) & 0xFF
+    nonzero = exp_field > 0
+    scaled = kr + (np.uint32(6) << 7) * (big[:, None] & nonzero)   # multiply by 2^6 in the exponent field
+    case.k_rope = scaled.astype(np.uint16)
+    cache, q_rot = oracle_cache(case)
+    # the inputs really do exceed the fast path's range: some head's later max is > 64 (log2) above its
+    # first 32-token max
+    L0 = int(case.seq_lens[0])
+    rows = O.gather_rows(cache, case.block_table, case.max_blocks_per_seq, 0, L0)
+    s = (O.bf16_to_f64(q_rot[0]) @ rows[:, 512:].T) / np.sqrt(192) * np.log2(np.e)
+    assert np.max(s[:, 64:].max(axis=1) - s[:, :32].max(axis=1)) > 64
+    dc, out, lse = run_decode(case, 128, 6)
+    ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
+                       case.w_uk, case.w_uv)
+    assert_close(out, ref, "growth")
+    assert np.max(np.abs(lse - rl)) <= LSE_ABS
