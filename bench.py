@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the absorbed-MLA decode step on one MI355X.
+
+Workload: decode B=32, n_h=128, d_c=512, d_R=64, d_nope=128, d_v=128, context 4096 per sequence,
+contiguous bf16 latent cache (576 elements per token), synthetic seeded inputs with the shapes of
+the DeepSeek-V2 dimensions. One step = the whole decode hot path on one batch:
+  mla_rope_append (the 32 new tokens: rotate k_R and q_R, write the rows)
+  -> mla_decode (q absorption through W_UK + split-KV attention over the latent cache)
+  -> mla_decode_combine (log-sum-exp merge of the splits + W_UV up-projection).
+Inputs are resident in HBM before timing starts. Several independent copies of the inputs are
+rotated so that the 256 MB Infinity Cache cannot hold one step's working set.
+
+Prints ONE JSON line. `value` is the step's algorithmic TFLOP/s; latent-KV GB/s, the dominant
+kernel's roofline fraction and the fp64 CPU oracle's rate (on the host's cores) ride along.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_04_amd", "csrc", "decode_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_units: str):
+    """HBM bytes per launch of the attention kernel from committed counter runs, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != per_launch_units:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_loop(torch, fn, n):
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(n):
+        fn(i)
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def cpu_baseline(case, budget_s):
+    """fp64 expanded-form oracle on whole sequences (all heads) of the same workload, until the
+    time budget is spent; rate in the metric's unit (algorithmic TFLOP/s of absorbed decode)."""
+    import numpy as np
+
+    from oracle import mla_oracle as O
+    from workloads import BF16_NAN
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
+    cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
+                             case.c_kv, case.k_rope)
+    q_rot = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(case.q_rope), case.q_positions()[:, None]))
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while done < case.batch and time.perf_counter() - t0 < budget_s:
+        O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot, case.w_uk,
+                 case.w_uv, seqs=[done])
+        flops += step_flops_one_seq(case, done)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {case.batch} sequences (all {case.n_heads} heads, L={int(case.seq_lens[0])}), "
+                      f"fp64 expanded form, {dt:.1f} s"}
+
+
+def step_flops_one_seq(case, b):
+    H = case.n_heads
+    L = int(case.seq_lens[b])
+    attn = L * H * (2 * 576 + 2 * 512)
+    proj = H * 2 * (128 * 512 * 2)  # absorption through W_UK and up-projection through W_UV
+    return float(attn + proj)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the decode hot path on one GPU only; run it with --gpus 1 "
+              f"(got --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from head_latent_attention_04_amd import lib
+    from head_latent_attention_04_amd.runner import DeviceCase
+    from workloads import make_config
+
+    torch.cuda.set_device(0)
+    lib.load()
+    props = torch.cuda.get_device_properties(0)
+    case = make_config(1)
+    B, H = case.batch, case.n_heads
+    L = int(case.seq_lens[0])
+    st, ns = lib.decode_plan(lib.make_dims(H), B, int(case.seq_lens.max()), props.multi_processor_count)
+
+    sets = []
+    for _ in range(max(1, args.sets)):
+        ds = DeviceCase(case)
+        ds.fill_history()
+        ds.prepare_step_inputs()
+        ds.alloc_decode(ns)
+        ds.append_new()
+        sets.append(ds)
+    torch.cuda.synchronize()
+    nsets = len(sets)
+
+    def step(i):
+        ds = sets[i % nsets]
+        ds.append_new(reset_q=False)   # the rotation repeats on the already-rotated query: same work
+        ds.decode(st, ns)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = time_loop(torch, step, args.steps)
+
+    # the dominant kernel alone: split-KV attention over the latent cache (absorbed queries ready)
+    for ds in sets:
+        ds.decode(st, ns, combine=False)
+    torch.cuda.synchronize()
+    qabs = [ds._ws[: B * H * 576 * 2].view(torch.int16) for ds in sets]
+
+    def attn(i):
+        ds = sets[i % nsets]
+        o_part, lse_part = ds.partials
+        lib.decode_absorbed(ds.dims, ds.cache, ds.seq_lens, qabs[i % nsets], st, ns, o_part, lse_part)
+
+    for i in range(args.warmup):
+        attn(i)
+    ms_attn = time_loop(torch, attn, args.steps)
+
+    def comb(i):
+        ds = sets[i % nsets]
+        o_part, lse_part = ds.partials
+        lib.decode_combine(ds.dims, B, ns, o_part, lse_part, ds.w_uv, ds.out, ds.lse)
+
+    ms_comb = time_loop(torch, comb, args.steps)
+
+    def rope(i):
+        sets[i % nsets].append_new(reset_q=False)
+
+    ms_rope = time_loop(torch, rope, args.steps)
+
+    tokens = int(case.seq_lens.sum())
+    flops = sum(step_flops_one_seq(case, b) for b in range(B))
+    cache_bytes = tokens * 1152
+    weight_bytes = 2 * H * 128 * 512 * 2
+    io_bytes = B * H * (128 + 64) * 2 + B * H * 128 * 2
+    step_bytes = cache_bytes + weight_bytes + io_bytes
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_gbps = cache_bytes / (ms_attn * 1e-3) / 1e9
+    workload = f"decode B={B} n_h={H} ctx={L} contiguous bf16 latent cache, split {ns}x{st} tokens"
+    traffic = measured_traffic(workload)
+
+    result = {
+        "metric": "absorbed MLA decode TFLOP/s + latent-KV GB/s, n_h=128, B=32, ctx 4K",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "global_batch": B, "seq_len": L, "n_heads": H, "d_c": 512, "d_rope": 64,
+                   "d_nope": 128, "d_v": 128, "input_sets_rotated": nsets},
+        "latent_kv_GBps": round(cache_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "total_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_roofline_frac_hbm": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_ms": {"rope_append": round(ms_rope, 5), "decode_attention": round(ms_attn, 5),
+                       "combine_wuv": round(ms_comb, 5)},
+        "roofline": {"kernel": "decode_mfma_kernel<4> (split-KV attention)", "bound": "hbm",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": cache_bytes,
+                     "mfma_tflops": round(tokens * H * (2 * 576 + 2 * 512) / (ms_attn * 1e-3) / 1e12, 1)},
+        "device": props.name,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

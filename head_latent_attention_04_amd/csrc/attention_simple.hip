@@ -1,4 +1,4 @@
-// Straightforward attention over the latent cache: one wave per (query row, head, key range).
+// Straightforward causal prefill attention over the latent cache: one wave per (query row, head).
 //
 // This is the plain formulation of the absorbed scores and the latent reduction
 // ("论文复现工坊 No.4", sections 2 and 4; "淺析DeepSeek多頭潛在注意力機制（MLA）", "MLA的數學原理"):
@@ -71,29 +71,6 @@ __device__ void attend_range(const CacheView& cache, int seq, int t0, int t1, co
 
 }  // namespace
 
-// grid (n_heads, num_splits, batch), block 64
-__global__ void __launch_bounds__(64) decode_simple_kernel(CacheView cache, int n_heads, const int32_t* __restrict__ seq_lens,
-                                                           const uint16_t* __restrict__ q_abs, float scale_log2,
-                                                           int split_tokens, int num_splits, float* __restrict__ o_partial,
-                                                           float* __restrict__ lse_partial) {
-  const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
-  __shared__ float q[kRow];
-  const uint16_t* qa = q_abs + ((int64_t)b * n_heads + h) * kRow;
-  for (int k = lane; k < kRow; k += 64) q[k] = bf16_to_f32(qa[k]);
-  __syncthreads();
-  const int L = seq_lens[b];
-  const int t0 = s * split_tokens;
-  const int t1 = min(L, t0 + split_tokens);
-  float o[8], m, l;
-  attend_range(cache, b, t0, t1, q, scale_log2, o, m, l);
-  const int64_t ps = ((int64_t)b * n_heads + h) * num_splits + s;
-  float inv = (l > 0.f) ? 1.f / l : 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) o_partial[ps * kDc + lane + 64 * k] = o[k] * inv;
-  if (lane == 0) lse_partial[ps] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
-}
-
 // grid (n_heads, total_q), block 64: query row j sees keys 0..pos_j.
 __global__ void __launch_bounds__(64) prefill_simple_kernel(CacheView cache, int batch, int n_heads,
                                                             const int32_t* __restrict__ seq_lens,
@@ -117,15 +94,6 @@ __global__ void __launch_bounds__(64) prefill_simple_kernel(CacheView cache, int
 #pragma unroll
   for (int k = 0; k < 8; ++k) o_lat[r * kDc + lane + 64 * k] = o[k] * inv;
   if (lane == 0) lse[r] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
-}
-
-hipError_t launch_decode_attention_simple(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
-                                   const uint16_t* q_abs, float scale, int split_tokens, int num_splits,
-                                   float* o_partial, float* lse_partial, hipStream_t stream) {
-  if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_simple_kernel, dim3(n_heads, num_splits, batch), dim3(64), 0, stream, cache, n_heads,
-                     seq_lens, q_abs, scale * kLog2e, split_tokens, num_splits, o_partial, lse_partial);
-  return hipGetLastError();
 }
 
 hipError_t launch_prefill_attention(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,

@@ -28,6 +28,14 @@ int check_cache(const mla_cache* c) {
   return MLA_OK;
 }
 
+int check_splits(const mla_dims* d, int32_t batch, int32_t split_tokens, int32_t num_splits) {
+  if (batch < 0 || batch > 65535) return MLA_ERR_BAD_ARG;
+  if (split_tokens <= 0 || split_tokens % d->block_size != 0) return MLA_ERR_BAD_ARG;
+  if (num_splits <= 0 || num_splits > 65535) return MLA_ERR_BAD_ARG;
+  if ((int64_t)split_tokens * num_splits > (int64_t)INT32_MAX) return MLA_ERR_BAD_ARG;
+  return MLA_OK;
+}
+
 mla::CacheView view(const mla_cache* c) { return mla::CacheView{c->data, c->block_table, c->max_blocks_per_seq}; }
 
 int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
@@ -107,10 +115,7 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if ((st = check_cache(cache)) != MLA_OK) return st;
-  if (batch < 0 || batch > 65535) return MLA_ERR_BAD_ARG;
-  if (split_tokens <= 0 || split_tokens % dims->block_size != 0) return MLA_ERR_BAD_ARG;
-  if (num_splits <= 0 || num_splits > 65535) return MLA_ERR_BAD_ARG;
-  if ((int64_t)split_tokens * num_splits > (int64_t)INT32_MAX) return MLA_ERR_BAD_ARG;
+  if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
   if (batch == 0) return MLA_OK;
   if (!seq_lens || !q_nope || !q_rope || !w_uk || !workspace || !o_partial || !lse_partial) return MLA_ERR_NULL;
   if (workspace_bytes < mla_decode_workspace_size(dims, batch)) return MLA_ERR_BAD_ARG;
@@ -118,6 +123,19 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   uint16_t* q_abs = static_cast<uint16_t*>(workspace);
   hipError_t e = mla::launch_absorb(batch, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  return launched(mla::launch_decode_attention(view(cache), batch, dims->n_heads, seq_lens, q_abs, dims->scale,
+                                               split_tokens, num_splits, o_partial, lse_partial, stream));
+}
+
+int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                        const uint16_t* q_abs, int32_t split_tokens, int32_t num_splits, float* o_partial,
+                        float* lse_partial, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!seq_lens || !q_abs || !o_partial || !lse_partial) return MLA_ERR_NULL;
   return launched(mla::launch_decode_attention(view(cache), batch, dims->n_heads, seq_lens, q_abs, dims->scale,
                                                split_tokens, num_splits, o_partial, lse_partial, stream));
 }

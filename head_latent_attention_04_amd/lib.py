@@ -49,6 +49,8 @@ EXPORTS = {
     "mla_decode_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp, _i32,
                                   _i32, _vp, _sz, _vp, _vp, _vp]),
+    "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
+                                           _i32, _vp, _vp, _vp]),
     "mla_decode_combine": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mla_chunked_prefill_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
     "mla_chunked_prefill": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
@@ -155,6 +157,18 @@ def decode(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split
         _ptr(o_partial, "o_partial", F32, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
     _check("mla_decode", st)
+
+
+def decode_absorbed(dims: MlaDims, cache: MlaCache, seq_lens, q_abs, split_tokens: int, num_splits: int, o_partial,
+                    lse_partial, stream=None):
+    B = seq_lens.numel()
+    H = dims.n_heads
+    st = load().mla_decode_absorbed(
+        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(q_abs, "q_abs", BF16, B * H * (dims.d_c + dims.d_rope)), split_tokens, num_splits,
+        _ptr(o_partial, "o_partial", F32, B * H * num_splits * dims.d_c),
+        _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
+    _check("mla_decode_absorbed", st)
 
 
 def decode_combine(dims: MlaDims, batch: int, num_splits: int, o_partial, lse_partial, w_uv, out, lse_out=None,

@@ -72,9 +72,11 @@ class DeviceCase:
         self.step_c = self.c_kv[idx].contiguous()
         self.step_k = self.k_rope[idx].contiguous()
 
-    def append_new(self, stream=None):
-        """The step's append: new tokens' rows go to the cache and their RoPE queries are rotated."""
-        self.q_rope.copy_(self.q_rope_raw)
+    def append_new(self, stream=None, reset_q: bool = True):
+        """The step's append: new tokens' rows go to the cache and their RoPE queries are rotated
+        (in place; reset_q first restores the un-rotated queries)."""
+        if reset_q:
+            self.q_rope.copy_(self.q_rope_raw)
         if not hasattr(self, "step_seq"):
             self.prepare_step_inputs()
         lib.rope_append(self.dims, self.cache, self.step_seq, self.step_pos, self.step_c, self.step_k, self.q_rope,

@@ -134,6 +134,18 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
                float* o_partial, float* lse_partial, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mla_decode_absorbed - mla_decode for callers that already hold the absorbed queries, e.g. with
+ * W_UK folded into the query up-projection ahead of time ("淺析DeepSeek多頭潛在注意力機制（MLA）",
+ * "MLA的數學原理": x_t (W_q W_k^T) is one precomputable product).
+ *   q_abs  [batch, n_heads, d_c + d_rope] bf16; row = [W_UK[h]^T q_nope (d_c) | q_R rotated at L-1]
+ * Everything else (split rule, outputs, empty splits, contracts) is exactly as for mla_decode;
+ * no workspace is needed.
+ * ------------------------------------------------------------------------------------------- */
+int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                        const uint16_t* q_abs, int32_t split_tokens, int32_t num_splits, float* o_partial,
+                        float* lse_partial, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mla_decode_combine - log-sum-exp merge of the split partials and the W_UV up-projection.
  * ("论文复现工坊 No.4", section 1: no K or V tensor is ever expanded; the value side is
  *  W_UV applied after the latent reduction.)

@@ -347,6 +347,16 @@ def decode_absorbed(cache, block_table, max_blocks, seq_lens, q_nope, q_rope, w_
     return out, lse
 
 
+def absorb_query(q_nope, q_rope, w_uk):
+    """The 576-wide absorbed query row per head, float64: [W_UK[h]^T q_nope[h] | q_R[h]].
+
+    ([P1] section 4: Q_absorbed = Q W_UK^T, scored directly against c^KV.)
+    q_nope [..., H, d_nope], q_rope [..., H, d_R] bf16 -> [..., H, d_c + d_R].
+    """
+    q_abs = np.einsum("hdc,...hd->...hc", bf16_to_f64(w_uk), bf16_to_f64(q_nope))
+    return np.concatenate([q_abs, bf16_to_f64(q_rope)], axis=-1)
+
+
 def decode_split_partials(cache, block_table, max_blocks, seq_lens, q_nope, q_rope, w_uk,
                           split_tokens: int, num_splits: int, seqs=None, heads=None):
     """Per-split latent partials of absorbed decode: split s covers tokens

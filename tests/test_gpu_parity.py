@@ -249,3 +249,26 @@ def test_decode_large_score_growth_uses_exact_path():
                        case.w_uk, case.w_uv)
     assert_close(out, ref, "growth")
     assert np.max(np.abs(lse - rl)) <= LSE_ABS
+
+
+def test_decode_absorbed_entry_point():
+    """mla_decode_absorbed, fed absorbed queries formed by the oracle (rounded to bf16), matches the
+    oracle's decode."""
+    say("[decode] absorbed-query entry point")
+    case = make_case("absorbed", 81, 64, [900, 64, 333], paged=True, spare_blocks=2)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.append_new()
+    st, ns = 256, 4
+    dc.alloc_decode(ns)
+    cache, q_rot = oracle_cache(case)
+    q_abs = O.f64_to_bf16(O.absorb_query(case.q_nope, q_rot, case.w_uk))
+    q_dev = torch.from_numpy(q_abs.view(np.int16)).cuda()
+    o_part, lse_part = dc.partials
+    lib.decode_absorbed(dc.dims, dc.cache, dc.seq_lens, q_dev, st, ns, o_part, lse_part)
+    lib.decode_combine(dc.dims, case.batch, ns, o_part, lse_part, dc.w_uv, dc.out, dc.lse)
+    torch.cuda.synchronize()
+    ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
+                       case.w_uk, case.w_uv)
+    assert_close(to_f64(dc.out), ref, "decode_absorbed")
+    assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
