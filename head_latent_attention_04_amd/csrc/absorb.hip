@@ -7,48 +7,101 @@
 // Output row layout [r, h, 0:576] = [q_abs (512) | q_rope (64)], bf16, i.e. the query side of a
 // 576-wide dot product with a cache row [c_KV | k_R].
 //
-// One work-group per (head, 32 rows): W_UK[h] (128 x 512) is streamed once per group of rows and
-// each of the 256 threads owns two latent columns for all 32 rows (fp32 accumulation).
+// Per head this is a small GEMM, computed transposed with bf16 MFMA:
+//   q_abs^T[c, r] = sum_d W_UK[h][d][c] q_nope[r, h, d]     (M = c, N = r, K = d)
+// One work-group per (head, half of the 512 latent columns, up to 128 rows). The 128 x 256 slice of
+// W_UK[h] is staged in LDS once (rows padded to 544 bytes so the transposed reads of 4 rows hit
+// different banks) and read with ds_read_b64_tr_b16 as the d-contiguous A operand; q_nope rows are
+// the B operand straight from global memory. fp32 accumulation, one bf16 rounding.
 #include "mla_internal.h"
 
 namespace mla {
 
-constexpr int kAbsRows = 32;
+namespace {
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
 
-__global__ void __launch_bounds__(256) absorb_kernel(int rows, int n_heads, const uint16_t* __restrict__ q_nope,
-                                                      const uint16_t* __restrict__ q_rope,
-                                                      const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs) {
+constexpr int kCols = 256;                 // latent columns per work-group
+constexpr int kPitch = kCols * 2 + 32;     // LDS row pitch in bytes (544)
+constexpr int kRowsPerWg = 128;            // 4 blocks of 32 rows
+
+__device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+}  // namespace
+
+__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, const uint16_t* __restrict__ q_nope,
+                                                          const uint16_t* __restrict__ q_rope,
+                                                          const uint16_t* __restrict__ w_uk,
+                                                          uint16_t* __restrict__ q_abs) {
+  __shared__ __attribute__((aligned(16))) char w_lds[kDnope * kPitch];
   const int h = blockIdx.x;
-  const int r0 = blockIdx.y * kAbsRows;
-  const int tid = threadIdx.x;
-  __shared__ float qs[kAbsRows][kDnope];
-  for (int i = tid; i < kAbsRows * kDnope; i += 256) {
-    int rr = i / kDnope, d = i % kDnope;
-    int r = r0 + rr;
-    qs[rr][d] = (r < rows) ? bf16_to_f32(q_nope[((int64_t)r * n_heads + h) * kDnope + d]) : 0.f;
+  const int ch = blockIdx.y;                 // column half
+  const int rbase = blockIdx.z * kRowsPerWg;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
+  lds_char* lds = (lds_char*)w_lds;
+
+  // stage W_UK[h][:, ch*256 : ch*256 + 256]
+  const uint16_t* wsrc = w_uk + (int64_t)h * kDnope * kDc + ch * kCols;
+  for (int i = tid; i < kDnope * (kCols / 8); i += 256) {
+    const int d = i / (kCols / 8), c8 = i % (kCols / 8);
+    *reinterpret_cast<uint4*>(w_lds + d * kPitch + c8 * 16) =
+        *reinterpret_cast<const uint4*>(wsrc + (int64_t)d * kDc + c8 * 8);
   }
-  __syncthreads();
-  float acc0[kAbsRows], acc1[kAbsRows];
-#pragma unroll
-  for (int rr = 0; rr < kAbsRows; ++rr) { acc0[rr] = 0.f; acc1[rr] = 0.f; }
-  const uint16_t* w = w_uk + (int64_t)h * kDnope * kDc;
-  for (int d = 0; d < kDnope; ++d) {
-    float w0 = bf16_to_f32(w[d * kDc + tid]);
-    float w1 = bf16_to_f32(w[d * kDc + tid + 256]);
-#pragma unroll
-    for (int rr = 0; rr < kAbsRows; ++rr) {
-      acc0[rr] = fmaf(qs[rr][d], w0, acc0[rr]);
-      acc1[rr] = fmaf(qs[rr][d], w1, acc1[rr]);
+  // the RoPE part of the row is copied unchanged (column half 0 does it)
+  if (ch == 0) {
+    for (int i = tid; i < kRowsPerWg * (kDr / 8); i += 256) {
+      const int r = rbase + i / (kDr / 8), c8 = i % (kDr / 8);
+      if (r < rows)
+        reinterpret_cast<uint4*>(q_abs + ((int64_t)r * n_heads + h) * kRow + kDc)[c8] =
+            reinterpret_cast<const uint4*>(q_rope + ((int64_t)r * n_heads + h) * kDr)[c8];
     }
   }
+  __syncthreads();
+
+  // A operand (W^T, d-contiguous): in 16-lane group g, lane i supplies row d0 + i/4 at column
+  // c0 + 4 (i%4); lane then holds W[d0 + j][c0 + i], j = 0..3.
+  const int i16 = lane & 15, g = lane >> 4;
+  const uint32_t abase = ((i16 >> 2) + 8 * kh) * kPitch + (16 * (g & 1) + 4 * (i16 & 3)) * 2;
+
+  for (int rb = 0; rb < kRowsPerWg; rb += 32) {
+    const int r0 = rbase + rb;
+    if (r0 >= rows) break;
+    // B operand: q_nope[r][h][16 ks + 8 kh .. +7], r = r0 + (lane & 31)
+    const int r = r0 + (lane & 31);
+    bf16x8 qb[8];
+    const uint4* qsrc = reinterpret_cast<const uint4*>(q_nope + ((int64_t)min(r, rows - 1) * n_heads + h) * kDnope);
 #pragma unroll
-  for (int rr = 0; rr < kAbsRows; ++rr) {
-    int r = r0 + rr;
-    if (r < rows) {
-      uint16_t* o = q_abs + ((int64_t)r * n_heads + h) * kRow;
-      o[tid] = f32_to_bf16(acc0[rr]);
-      o[tid + 256] = f32_to_bf16(acc1[rr]);
-      if (tid < kDr) o[kDc + tid] = q_rope[((int64_t)r * n_heads + h) * kDr + tid];
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = qsrc[2 * ks + kh];
+      if (r >= rows) v = make_uint4(0, 0, 0, 0);
+      qb[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int cbi = 0; cbi < 2; ++cbi) {
+      const int cb = (wave * 2 + cbi) * 32;  // column block within the half
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const lds_char* p = lds + abase + (16 * ks) * kPitch + cb * 2;
+        const i16x4 lo = lds_tr16(p);
+        const i16x4 hi = lds_tr16(p + 4 * kPitch);
+        const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qb[ks], acc, 0, 0, 0);
+      }
+      if (r < rows) {
+        uint16_t* dst = q_abs + ((int64_t)r * n_heads + h) * kRow + ch * kCols + cb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 8 * q + 4 * kh;
+          const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(dst + c) = make_uint2(w0, w1);
+        }
+      }
     }
   }
 }
@@ -56,8 +109,10 @@ __global__ void __launch_bounds__(256) absorb_kernel(int rows, int n_heads, cons
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
                          const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  dim3 grid(n_heads, (rows + kAbsRows - 1) / kAbsRows);
-  hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), 0, stream, rows, n_heads, q_nope, q_rope, w_uk, q_abs);
+  const int zb = (rows + kRowsPerWg - 1) / kRowsPerWg;
+  if (zb > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(n_heads, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, q_nope,
+                     q_rope, w_uk, q_abs);
   return hipGetLastError();
 }
 

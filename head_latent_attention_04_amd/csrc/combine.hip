@@ -6,73 +6,121 @@
 // token ("论文复现工坊 No.4", section 1; "Multi-Head Latent Attention: DeepSeek V2/V3 工程视角",
 // section 四: the W_UV up-projection or its absorbed equivalent).
 //
-// One work-group per (head, 16 sequences): the merged latents go to LDS in fp32, and each thread
-// produces one output column for 8 sequences, reading W_UV[h] once per work-group.
+// One work-group per (head, 32 sequences), 4 waves:
+//   1. merge: wave w merges latent columns [128 w, 128 w + 128) for the 32 sequences (fp32) and
+//      stores them in LDS as a bf16 pair hi + lo (hi = bf16(o), lo = bf16(o - hi)), which carries
+//      the merged latent to the MFMA with about 16 significant bits;
+//   2. up-projection with bf16 MFMA: out^T[v, b] = W_UV[h][v, :] . o_lat[b, :] for the wave's 32
+//      output columns v (M = v, N = b, K = c), hi and lo accumulated into the same fp32 tile.
 #include "mla_internal.h"
 
 namespace mla {
 
-constexpr int kCombRows = 16;
+namespace {
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
 
-__global__ void __launch_bounds__(256) combine_simple_kernel(int batch, int n_heads, int num_splits,
-                                                             const float* __restrict__ o_partial,
-                                                             const float* __restrict__ lse_partial,
-                                                             const uint16_t* __restrict__ w_uv,
-                                                             uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+constexpr int kRowsPerWg = 32;
+constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded (conflict-free b128 reads)
+}  // namespace
+
+__global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_heads, int num_splits,
+                                                           const float* __restrict__ o_partial,
+                                                           const float* __restrict__ lse_partial,
+                                                           const uint16_t* __restrict__ w_uv,
+                                                           uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  __shared__ __attribute__((aligned(16))) char hi_lds[kRowsPerWg * kPitch];
+  __shared__ __attribute__((aligned(16))) char lo_lds[kRowsPerWg * kPitch];
   const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kCombRows;
-  const int tid = threadIdx.x;
-  __shared__ float olat[kCombRows][kDc];
-  for (int rr = 0; rr < kCombRows; ++rr) {
-    const int b = b0 + rr;
-    if (b >= batch) {
-      for (int c = tid; c < kDc; c += 256) olat[rr][c] = 0.f;
-      continue;
-    }
-    const int64_t base = ((int64_t)b * n_heads + h) * num_splits;
-    // max and sum of exp over splits (every thread computes the same scalars)
+  const int b0 = blockIdx.y * kRowsPerWg;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
+  const int b = b0 + (lane & 31);
+  const bool bok = b < batch;
+
+  // ---- 1. merge the splits of (b, h): lane owns latent columns 128 wave + 64 kh + [0, 64)
+  {
+    const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
     float m = -INFINITY;
     for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
     float z = 0.f;
     if (m != -INFINITY)
-      for (int s = 0; s < num_splits; ++s) z += expf(lse_partial[base + s] - m);
-    if (tid == 0 && lse_out) lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + logf(z);
-    for (int c = tid; c < kDc; c += 256) {
-      float acc = 0.f;
-      if (m != -INFINITY) {
-        for (int s = 0; s < num_splits; ++s) {
-          float ls = lse_partial[base + s];
-          if (ls != -INFINITY) acc = fmaf(expf(ls - m) / z, o_partial[(base + s) * kDc + c], acc);
+      for (int s = 0; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
+    if (wave == 0 && kh == 0 && bok && lse_out)
+      lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
+    const float inv_z = (m == -INFINITY) ? 0.f : 1.f / z;
+    const int c0 = 128 * wave + 64 * kh;
+    float acc[64];
+#pragma unroll
+    for (int k = 0; k < 64; ++k) acc[k] = 0.f;
+    if (bok && m != -INFINITY) {
+      for (int s = 0; s < num_splits; ++s) {
+        const float ls = lse_partial[base + s];
+        if (ls == -INFINITY) continue;
+        const float wgt = __expf(ls - m) * inv_z;
+        const float4* src = reinterpret_cast<const float4*>(o_partial + (base + s) * kDc + c0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float4 v = src[k];
+          acc[4 * k] = fmaf(wgt, v.x, acc[4 * k]);
+          acc[4 * k + 1] = fmaf(wgt, v.y, acc[4 * k + 1]);
+          acc[4 * k + 2] = fmaf(wgt, v.z, acc[4 * k + 2]);
+          acc[4 * k + 3] = fmaf(wgt, v.w, acc[4 * k + 3]);
         }
       }
-      olat[rr][c] = acc;
+    }
+    char* hrow = hi_lds + (lane & 31) * kPitch + c0 * 2;
+    char* lrow = lo_lds + (lane & 31) * kPitch + c0 * 2;
+#pragma unroll
+    for (int k = 0; k < 64; k += 8) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint16_t h0 = f32_to_bf16(acc[k + e]), h1 = f32_to_bf16(acc[k + e + 1]);
+        const uint16_t l0 = f32_to_bf16(acc[k + e] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16(acc[k + e + 1] - bf16_to_f32(h1));
+        hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      *reinterpret_cast<uint4*>(hrow + k * 2) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(lrow + k * 2) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
   }
   __syncthreads();
-  const int v = tid % kDv;
-  const int half = tid / kDv;  // sequences half*8 .. half*8+7
-  const uint16_t* w = w_uv + ((int64_t)h * kDv + v) * kDc;
-  float acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  for (int c = 0; c < kDc; ++c) {
-    float wv = bf16_to_f32(w[c]);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = fmaf(wv, olat[half * 8 + k][c], acc[k]);
+
+  // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32): A = W_UV rows (global), B = merged latent (LDS)
+  const int v = 32 * wave + (lane & 31);
+  const uint4* wrow = reinterpret_cast<const uint4*>(w_uv + ((int64_t)h * kDv + v) * kDc + 8 * kh);
+  const lds_char* hb = (lds_char*)hi_lds + (lane & 31) * kPitch + 16 * kh;
+  const lds_char* lb = (lds_char*)lo_lds + (lane & 31) * kPitch + 16 * kh;
+  f32x16 acc = f32x16{};
+#pragma unroll 8
+  for (int ks = 0; ks < kDc / 16; ++ks) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, wrow[2 * ks]);
+    const bf16x8 bh = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(hb + 32 * ks);
+    const bf16x8 bl = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lb + 32 * ks);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
   }
+  // D: lane holds sequence b (column) and output dims 32 wave + 8 q + 4 kh + (0..3)
+  if (bok) {
+    uint16_t* dst = out + ((int64_t)b * n_heads + h) * kDv + 32 * wave;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    int b = b0 + half * 8 + k;
-    if (b < batch) out[((int64_t)b * n_heads + h) * kDv + v] = f32_to_bf16(acc[k]);
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
+      *reinterpret_cast<uint2*>(dst + 8 * q + 4 * kh) = make_uint2(w0, w1);
+    }
   }
 }
 
 hipError_t launch_combine(int batch, int n_heads, int num_splits, const float* o_partial, const float* lse_partial,
                           const uint16_t* w_uv, uint16_t* out, float* lse_out, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  dim3 grid(n_heads, (batch + kCombRows - 1) / kCombRows);
-  hipLaunchKernelGGL(combine_simple_kernel, grid, dim3(256), 0, stream, batch, n_heads, num_splits, o_partial,
-                     lse_partial, w_uv, out, lse_out);
+  const int yb = (batch + kRowsPerWg - 1) / kRowsPerWg;
+  if (yb > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_mfma_kernel, dim3(n_heads, yb), dim3(256), 0, stream, batch, n_heads, num_splits,
+                     o_partial, lse_partial, w_uv, out, lse_out);
   return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -135,8 +137,10 @@ __device__ __forceinline__ void score_mfma_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+// max of a value over the lane pair (l, l ^ 32), returned to both lanes (v_permlane32_swap, no LDS)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // XCD-aware work order: consecutive logical work items land on the same XCD (work-groups are
@@ -288,44 +292,47 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_head_groups, const int32_
     for (int sub = 0; sub < 2; ++sub) {
       if (sub * 32 >= valid) break;
       const uint32_t soff = bufoff + sub * 32 * 16;
-      // ---- scores S^T[32 tokens x 32 heads], operand loads two steps ahead of the MFMA
+      // ---- scores S^T[32 tokens x 32 heads]
       f32x16 sacc;
       const lds_char* a_lo = lds + (abase + soff);
       const lds_char* a_hi = lds + (abase + soff + 65536);
       auto a_ld = [&](int ks) { return ks < 32 ? lds_b128(a_lo + ks * 2048) : lds_b128(a_hi + (ks - 32) * 2048); };
-      bf16x8 a_cur = a_ld(0);
-      bf16x8 a_nxt = a_ld(1);
+      constexpr int kAhead = 4;  // operand loads issued this many MFMAs ahead
+      bf16x8 a_buf[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) a_buf[i] = a_ld(i);
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
-        bf16x8 a_far = a_nxt;
-        if (ks + 2 < 36) a_far = a_ld(ks + 2);
+        const bf16x8 a = a_buf[ks % kAhead];
+        if (ks + kAhead < 36) a_buf[ks % kAhead] = a_ld(ks + kAhead);
         if (ks == 0)
-          score_mfma_first(sacc, a_cur, qreg[0]);
+          score_mfma_first(sacc, a, qreg[0]);
         else
-          score_mfma(sacc, a_cur, qreg[ks]);
-        a_cur = a_nxt;
-        a_nxt = a_far;
+          score_mfma(sacc, a, qreg[ks]);
       }
       score_mfma_drain(sacc);
       // ---- softmax weights; element j is token 32*sub + 8*(j>>2) + 4*kh + (j&3)
-      float mx = -INFINITY;
+      if (valid - 32 * sub < 32) {  // only the block's last, partly filled sub-tile needs a mask
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int tk = 32 * sub + 8 * (j >> 2) + 4 * kh + (j & 3);
-        const float v = tk < valid ? sacc[j] * scale_log2 : -INFINITY;
-        sacc[j] = v;
-        mx = fmaxf(mx, v);
+        for (int j = 0; j < 16; ++j) {
+          const int tk = 32 * sub + 8 * (j >> 2) + 4 * kh + (j & 3);
+          if (tk >= valid) sacc[j] = -INFINITY;
+        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = sacc[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+      mx = pair_max(mx) * scale_log2;  // scale > 0: the max commutes with it
       if (m_ref == -INFINITY) m_ref = mx;
       overflow |= mx > m_ref + kMaxExcess;
       uint32_t pw[8];
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
-        const float p0 = exp2f(sacc[j] - m_ref);
-        const float p1 = exp2f(sacc[j + 1] - m_ref);
+        // raw v_exp_f32: weights below 2^-126 flush to zero, which a softmax weight can afford
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], scale_log2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], scale_log2, -m_ref));
         lsum += p0 + p1;
-        pw[j >> 1] = pack_bf16x2(p0, p1);
+        pw[j >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
       }
       // ---- O^T[d, head] += C^T[d, token] P^T[token, head]; transposed reads one block ahead
 #pragma unroll
