@@ -46,10 +46,19 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
 
   // stage W_UK[h][:, ch*256 : ch*256 + 256]
   const uint16_t* wsrc = w_uk + (int64_t)h * kDnope * kDc + ch * kCols;
-  for (int i = tid; i < kDnope * (kCols / 8); i += 256) {
-    const int d = i / (kCols / 8), c8 = i % (kCols / 8);
-    *reinterpret_cast<uint4*>(w_lds + d * kPitch + c8 * 16) =
-        *reinterpret_cast<const uint4*>(wsrc + (int64_t)d * kDc + c8 * 8);
+  {
+    constexpr int kPer = kDnope * (kCols / 8) / 256;  // 16 loads per thread, all issued before any store
+    uint4 v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + 256 * k, d = i / (kCols / 8), c8 = i % (kCols / 8);
+      v[k] = *reinterpret_cast<const uint4*>(wsrc + (int64_t)d * kDc + c8 * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + 256 * k, d = i / (kCols / 8), c8 = i % (kCols / 8);
+      *reinterpret_cast<uint4*>(w_lds + d * kPitch + c8 * 16) = v[k];
+    }
   }
   // the RoPE part of the row is copied unchanged (column half 0 does it)
   if (ch == 0) {

@@ -1,17 +1,18 @@
 // Split-KV combine and value up-projection.
 //
-// The partials of one (sequence, head) are merged with their log-sum-exps (the same softmax,
+// The partials (bf16) of one (sequence, head) are merged with their log-sum-exps (the same softmax,
 // taken in pieces): lse = ln sum_s exp(lse_s), o_lat = sum_s exp(lse_s - lse) o_s. The merged
 // latent is then up-projected, out[h] = W_UV[h] o_lat: the value side is never expanded per
 // token ("论文复现工坊 No.4", section 1; "Multi-Head Latent Attention: DeepSeek V2/V3 工程视角",
 // section 四: the W_UV up-projection or its absorbed equivalent).
 //
-// One work-group per (head, 32 sequences), 4 waves:
-//   1. merge: wave w merges latent columns [128 w, 128 w + 128) for the 32 sequences (fp32) and
+// One work-group per (head, 16 sequences), 4 waves:
+//   1. merge: wave w merges latent columns [128 w, 128 w + 128) for the 16 sequences (fp32) and
 //      stores them in LDS as a bf16 pair hi + lo (hi = bf16(o), lo = bf16(o - hi)), which carries
 //      the merged latent to the MFMA with about 16 significant bits;
 //   2. up-projection with bf16 MFMA: out^T[v, b] = W_UV[h][v, :] . o_lat[b, :] for the wave's 32
-//      output columns v (M = v, N = b, K = c), hi and lo accumulated into the same fp32 tile.
+//      output columns v (M = v, N = b padded to 32 with zero rows, K = c), hi and lo accumulated
+//      into the same fp32 tile.
 #include "mla_internal.h"
 
 namespace mla {
@@ -21,22 +22,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kRowsPerWg = 32;
+constexpr int kRowsPerWg = 16;  // sequences per work-group (MFMA columns 16..31 unused)
 constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded (conflict-free b128 reads)
 }  // namespace
 
 __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_heads, int num_splits,
-                                                           const float* __restrict__ o_partial,
+                                                           const uint16_t* __restrict__ o_partial,
                                                            const float* __restrict__ lse_partial,
                                                            const uint16_t* __restrict__ w_uv,
                                                            uint16_t* __restrict__ out, float* __restrict__ lse_out) {
-  __shared__ __attribute__((aligned(16))) char hi_lds[kRowsPerWg * kPitch];
-  __shared__ __attribute__((aligned(16))) char lo_lds[kRowsPerWg * kPitch];
+  __shared__ __attribute__((aligned(16))) char hi_lds[32 * kPitch];
+  __shared__ __attribute__((aligned(16))) char lo_lds[32 * kPitch];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kRowsPerWg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
   const int b = b0 + (lane & 31);
-  const bool bok = b < batch;
+  const bool bok = (lane & 31) < kRowsPerWg && b < batch;
 
   // ---- 1. merge the splits of (b, h): lane owns latent columns 128 wave + 64 kh + [0, 64)
   {
@@ -54,18 +55,31 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
 #pragma unroll
     for (int k = 0; k < 64; ++k) acc[k] = 0.f;
     if (bok && m != -INFINITY) {
-      for (int s = 0; s < num_splits; ++s) {
-        const float ls = lse_partial[base + s];
-        if (ls == -INFINITY) continue;
-        const float wgt = __expf(ls - m) * inv_z;
-        const float4* src = reinterpret_cast<const float4*>(o_partial + (base + s) * kDc + c0);
+      // splits four at a time, every load of a group issued before the first multiply-add
+      for (int s0 = 0; s0 < num_splits; s0 += 4) {
+        uint4 v[4][8];
+        float wgt[4];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float4 v = src[k];
-          acc[4 * k] = fmaf(wgt, v.x, acc[4 * k]);
-          acc[4 * k + 1] = fmaf(wgt, v.y, acc[4 * k + 1]);
-          acc[4 * k + 2] = fmaf(wgt, v.z, acc[4 * k + 2]);
-          acc[4 * k + 3] = fmaf(wgt, v.w, acc[4 * k + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const int s = s0 + q;
+          const float ls = s < num_splits ? lse_partial[base + s] : -INFINITY;
+          wgt[q] = ls == -INFINITY ? 0.f : __expf(ls - m) * inv_z;
+          const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(s, num_splits - 1)) * kDc + c0);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[q][k] = src[k];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (wgt[q] == 0.f) continue;  // empty split (or past the end): contributes nothing
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t wv[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[8 * k + 2 * e] = fmaf(wgt[q], __uint_as_float(wv[e] << 16), acc[8 * k + 2 * e]);
+              acc[8 * k + 2 * e + 1] = fmaf(wgt[q], __uint_as_float(wv[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+            }
+          }
         }
       }
     }
@@ -114,8 +128,9 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
   }
 }
 
-hipError_t launch_combine(int batch, int n_heads, int num_splits, const float* o_partial, const float* lse_partial,
-                          const uint16_t* w_uv, uint16_t* out, float* lse_out, hipStream_t stream) {
+hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t* o_partial,
+                          const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
+                          hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   const int yb = (batch + kRowsPerWg - 1) / kRowsPerWg;
   if (yb > 65535) return hipErrorInvalidValue;

@@ -10,6 +10,8 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int32_t kMaxSplitTokens = 0x7FFFFFC0;  // largest block multiple: one split per row
+
 int check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_NULL;
   if (d->n_heads <= 0 || d->d_c <= 0 || d->d_rope <= 0 || d->d_nope <= 0 || d->d_v <= 0 || d->block_size <= 0)
@@ -49,7 +51,7 @@ PrefillWorkspace prefill_layout(const mla_dims* d, int32_t total_q) {
   size_t rows = (size_t)(total_q > 0 ? total_q : 0) * (size_t)d->n_heads;
   w.q_abs = 0;
   w.o_lat = align256(rows * mla::kRow * 2);
-  w.lse = w.o_lat + align256(rows * mla::kDc * 4);
+  w.lse = w.o_lat + align256(rows * mla::kDc * 2);
   w.total = w.lse + align256(rows * 4);
   return w;
 }
@@ -110,7 +112,7 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch) {
 
 int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
                const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int32_t split_tokens,
-               int32_t num_splits, void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial,
+               int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* o_partial, float* lse_partial,
                hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
@@ -123,12 +125,12 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   uint16_t* q_abs = static_cast<uint16_t*>(workspace);
   hipError_t e = mla::launch_absorb(batch, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
-  return launched(mla::launch_decode_attention(view(cache), batch, dims->n_heads, seq_lens, q_abs, dims->scale,
-                                               split_tokens, num_splits, o_partial, lse_partial, stream));
+  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs,
+                                        dims->scale, split_tokens, num_splits, o_partial, lse_partial, stream));
 }
 
 int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
-                        const uint16_t* q_abs, int32_t split_tokens, int32_t num_splits, float* o_partial,
+                        const uint16_t* q_abs, int32_t split_tokens, int32_t num_splits, uint16_t* o_partial,
                         float* lse_partial, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
@@ -136,11 +138,11 @@ int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t ba
   if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
   if (batch == 0) return MLA_OK;
   if (!seq_lens || !q_abs || !o_partial || !lse_partial) return MLA_ERR_NULL;
-  return launched(mla::launch_decode_attention(view(cache), batch, dims->n_heads, seq_lens, q_abs, dims->scale,
-                                               split_tokens, num_splits, o_partial, lse_partial, stream));
+  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs,
+                                        dims->scale, split_tokens, num_splits, o_partial, lse_partial, stream));
 }
 
-int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const float* o_partial,
+int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const uint16_t* o_partial,
                        const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
                        hipStream_t stream) {
   int st = check_dims(dims);
@@ -172,12 +174,15 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
   if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
   char* ws = static_cast<char*>(workspace);
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + lay.q_abs);
-  float* o_lat = reinterpret_cast<float*>(ws + lay.o_lat);
+  uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + lay.o_lat);
   float* lse = reinterpret_cast<float*>(ws + lay.lse);
   hipError_t e = mla::launch_absorb(total_q, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
-  e = mla::launch_prefill_attention(view(cache), batch, dims->n_heads, seq_lens, cu_q_lens, total_q, max_q_len, q_abs,
-                                    dims->scale, o_lat, lse, stream);
+  // one query token per row; the whole causal key range of a row is one split (split_tokens is
+  // only the split length, so any multiple of the block covering the longest sequence works)
+  (void)max_q_len;
+  e = mla::launch_attention(view(cache), total_q, dims->n_heads, seq_lens, cu_q_lens, batch, q_abs, dims->scale,
+                            kMaxSplitTokens, 1, o_lat, lse, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   return launched(mla::launch_combine(total_q, dims->n_heads, 1, o_lat, lse, w_uv, out, lse_out, stream));
 }

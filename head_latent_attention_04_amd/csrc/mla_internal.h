@@ -58,18 +58,18 @@ hipError_t launch_rope_append(const CacheView& cache, int n_heads, int num_token
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
                          const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream);
 
-// Split-KV decode attention over the latent cache (rows = heads of one query token).
-hipError_t launch_decode_attention(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
-                                   const uint16_t* q_abs, float scale, int split_tokens, int num_splits,
-                                   float* o_partial, float* lse_partial, hipStream_t stream);
-
-// Causal prefill attention producing normalised latent outputs and lse per (query, head).
-hipError_t launch_prefill_attention(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
-                                    const int32_t* cu_q_lens, int total_q, int max_q_len, const uint16_t* q_abs,
-                                    float scale, float* o_lat, float* lse, hipStream_t stream);
+// Split-KV attention over the latent cache with bf16 MFMA. Row r of the work is one query token:
+// decode (cu_q_lens == nullptr): row r is sequence r and sees its seq_lens[r] tokens; prefill: row j
+// is query token j (sequence located through cu_q_lens[0..batch]) and sees tokens 0..its position.
+// Writes per (row, head, split) the normalised latent partial (bf16, [rows, n_heads, splits, 512])
+// and its log-sum-exp (fp32, natural log).
+hipError_t launch_attention(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
+                            const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, float scale, int split_tokens,
+                            int num_splits, uint16_t* o_partial, float* lse_partial, hipStream_t stream);
 
 // LSE merge over splits + W_UV up-projection.
-hipError_t launch_combine(int batch, int n_heads, int num_splits, const float* o_partial, const float* lse_partial,
-                          const uint16_t* w_uv, uint16_t* out, float* lse_out, hipStream_t stream);
+hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t* o_partial,
+                          const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
+                          hipStream_t stream);
 
 }  // namespace mla

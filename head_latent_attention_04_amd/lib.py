@@ -154,7 +154,7 @@ def decode(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split
         _ptr(q_nope, "q_nope", BF16, B * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, B * H * dims.d_rope),
         _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), split_tokens, num_splits,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _ptr(o_partial, "o_partial", F32, B * H * num_splits * dims.d_c),
+        _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
     _check("mla_decode", st)
 
@@ -166,7 +166,7 @@ def decode_absorbed(dims: MlaDims, cache: MlaCache, seq_lens, q_abs, split_token
     st = load().mla_decode_absorbed(
         ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
         _ptr(q_abs, "q_abs", BF16, B * H * (dims.d_c + dims.d_rope)), split_tokens, num_splits,
-        _ptr(o_partial, "o_partial", F32, B * H * num_splits * dims.d_c),
+        _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
     _check("mla_decode_absorbed", st)
 
@@ -175,7 +175,7 @@ def decode_combine(dims: MlaDims, batch: int, num_splits: int, o_partial, lse_pa
                    stream=None):
     H = dims.n_heads
     st = load().mla_decode_combine(
-        ctypes.byref(dims), batch, num_splits, _ptr(o_partial, "o_partial", F32, batch * H * num_splits * dims.d_c),
+        ctypes.byref(dims), batch, num_splits, _ptr(o_partial, "o_partial", BF16, batch * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, batch * H * num_splits),
         _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c), _ptr(out, "out", BF16, batch * H * dims.d_v),
         _ptr(lse_out, "lse_out", F32, batch * H), _stream(stream))

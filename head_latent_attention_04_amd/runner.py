@@ -93,7 +93,7 @@ class DeviceCase:
             self._ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
         key = (num_splits,)
         if self._part is None or self._part[0] != key:
-            self._part = (key, torch.empty((B, H, num_splits, lib.D_C), dtype=torch.float32, device=self.device),
+            self._part = (key, torch.empty((B, H, num_splits, lib.D_C), dtype=torch.int16, device=self.device),
                           torch.empty((B, H, num_splits), dtype=torch.float32, device=self.device))
         self.out = torch.empty((B, H, lib.D_V), dtype=torch.int16, device=self.device)
         self.lse = torch.empty((B, H), dtype=torch.float32, device=self.device)

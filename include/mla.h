@@ -118,20 +118,20 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch);
  *   q_abs[h]    = W_UK[h]^T q_nope[b, h]                   (d_c, rounded to bf16)
  *   s_t         = scale * (q_abs[h] . c_t + q_rope[b, h] . kR_t)
  *   lse_partial[b, h, s] = ln sum_t exp(s_t)                (-inf for an empty split)
- *   o_partial[b, h, s, :] = sum_t exp(s_t - lse_partial) c_t  (0 for an empty split)
+ *   o_partial[b, h, s, :] = sum_t exp(s_t - lse_partial) c_t  (rounded to bf16; 0 for an empty split)
  *   seq_lens     [batch] int32, 0 <= L <= num_splits * split_tokens
  *   q_nope       [batch, n_heads, d_nope] bf16
  *   q_rope       [batch, n_heads, d_rope] bf16, already rotated at position L-1
  *   w_uk         [n_heads, d_nope, d_c] bf16 (row d of head h maps c to the key's element d)
  *   split_tokens multiple of block_size, > 0; num_splits > 0
  *   workspace    >= mla_decode_workspace_size(dims, batch) bytes, 256-byte aligned
- *   o_partial    [batch, n_heads, num_splits, d_c] fp32
+ *   o_partial    [batch, n_heads, num_splits, d_c] bf16 (a softmax-weighted mean of c rows)
  *   lse_partial  [batch, n_heads, num_splits] fp32
  * ------------------------------------------------------------------------------------------- */
 int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
                const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
                int32_t split_tokens, int32_t num_splits, void* workspace, size_t workspace_bytes,
-               float* o_partial, float* lse_partial, hipStream_t stream);
+               uint16_t* o_partial, float* lse_partial, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_decode_absorbed - mla_decode for callers that already hold the absorbed queries, e.g. with
@@ -142,7 +142,7 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
  * no workspace is needed.
  * ------------------------------------------------------------------------------------------- */
 int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
-                        const uint16_t* q_abs, int32_t split_tokens, int32_t num_splits, float* o_partial,
+                        const uint16_t* q_abs, int32_t split_tokens, int32_t num_splits, uint16_t* o_partial,
                         float* lse_partial, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
@@ -150,12 +150,12 @@ int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t ba
  * ("论文复现工坊 No.4", section 1: no K or V tensor is ever expanded; the value side is
  *  W_UV applied after the latent reduction.)
  *   lse[b,h]   = ln sum_s exp(lse_partial[b,h,s])        (-inf if every split is empty)
- *   o_lat      = sum_s exp(lse_partial[b,h,s] - lse[b,h]) o_partial[b,h,s,:]   (fp32)
+ *   o_lat      = sum_s exp(lse_partial[b,h,s] - lse[b,h]) o_partial[b,h,s,:]   (fp32 accumulation)
  *   out[b,h,:] = W_UV[h] o_lat                             (bf16; 0 if every split is empty)
  *   w_uv    [n_heads, d_v, d_c] bf16;  out [batch, n_heads, d_v] bf16
  *   lse_out [batch, n_heads] fp32, natural log (may be NULL)
  * ------------------------------------------------------------------------------------------- */
-int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const float* o_partial,
+int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const uint16_t* o_partial,
                        const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
                        hipStream_t stream);
 

@@ -120,18 +120,20 @@ def test_partials_and_combine_match_oracle():
     cache, q_rot = oracle_cache(case)
     o_ref, l_ref = O.decode_split_partials(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens,
                                            case.q_nope, q_rot, case.w_uk, st, ns)
-    o_got, l_got = (t.cpu().numpy().astype(np.float64) for t in dc.partials)
+    o_got = to_f64(dc.partials[0])
+    l_got = dc.partials[1].cpu().numpy().astype(np.float64)
     empty = np.isneginf(l_ref)
     assert np.array_equal(np.isneginf(l_got), empty)
     assert np.all(o_got[empty] == 0)
     assert_close(o_got[~empty], o_ref[~empty], "o_partial")
     assert np.max(np.abs(l_got[~empty] - l_ref[~empty])) <= LSE_ABS
-    # combine alone, fed the oracle's partials
-    o_in = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+    # combine alone, fed the oracle's partials rounded to bf16 (the partial format)
+    o_bf = O.f64_to_bf16(np.where(empty[..., None], 0.0, o_ref))
+    o_in = torch.from_numpy(o_bf.view(np.int16)).cuda()
     l_in = torch.from_numpy(l_ref.astype(np.float32)).cuda()
     lib.decode_combine(dc.dims, case.batch, ns, o_in, l_in, dc.w_uv, dc.out, dc.lse)
     torch.cuda.synchronize()
-    ref, rl = O.combine(o_ref, l_ref, case.w_uv)
+    ref, rl = O.combine(O.bf16_to_f64(o_bf), l_ref, case.w_uv)
     assert_close(to_f64(dc.out), ref, "combine")
     assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
 
