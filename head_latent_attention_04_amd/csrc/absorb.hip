@@ -4,8 +4,9 @@
 // (Q_absorbed = Q W_UK^T) and the product is scored directly against the cached latent c^KV;
 // "淺析DeepSeek多頭潛在注意力機制（MLA）", "MLA的數學原理": x_t (W_q W_k^T) c_i^T.
 //
-// Output row layout [r, h, 0:576] = [q_abs (512) | q_rope (64)], bf16, i.e. the query side of a
-// 576-wide dot product with a cache row [c_KV | k_R].
+// Output element (r, h, 0:576) = [q_abs (512) | q_rope (64)], bf16, i.e. the query side of a
+// 576-wide dot product with a cache row [c_KV | k_R], stored in the attention kernel's operand order
+// (q_perm_offset; the padding heads of the last 32-head tile are written as zeros).
 //
 // Per head this is a small GEMM, computed transposed with bf16 MFMA:
 //   q_abs^T[c, r] = sum_d W_UK[h][d][c] q_nope[r, h, d]     (M = c, N = r, K = d)
@@ -42,7 +43,18 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
   const int ch = blockIdx.y;                 // column half
   const int rbase = blockIdx.z * kRowsPerWg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
+  const int tiles = q_tiles(n_heads);
   lds_char* lds = (lds_char*)w_lds;
+
+  if (h >= n_heads) {  // padding head of the last tile: zero query (columns of this half, RoPE part in half 0)
+    const int cols = ch == 0 ? kCols + kDr : kCols;
+    for (int i = tid; i < kRowsPerWg * (cols / 8); i += 256) {
+      const int r = rbase + i / (cols / 8), c8 = i % (cols / 8);
+      const int d = c8 * 8 < kCols ? ch * kCols + c8 * 8 : kDc + (c8 * 8 - kCols);
+      if (r < rows) *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, d)) = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
 
   // stage W_UK[h][:, ch*256 : ch*256 + 256]
   const uint16_t* wsrc = w_uk + (int64_t)h * kDnope * kDc + ch * kCols;
@@ -65,7 +77,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
     for (int i = tid; i < kRowsPerWg * (kDr / 8); i += 256) {
       const int r = rbase + i / (kDr / 8), c8 = i % (kDr / 8);
       if (r < rows)
-        reinterpret_cast<uint4*>(q_abs + ((int64_t)r * n_heads + h) * kRow + kDc)[c8] =
+        *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, kDc + 8 * c8)) =
             reinterpret_cast<const uint4*>(q_rope + ((int64_t)r * n_heads + h) * kDr)[c8];
     }
   }
@@ -102,13 +114,12 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qb[ks], acc, 0, 0, 0);
       }
       if (r < rows) {
-        uint16_t* dst = q_abs + ((int64_t)r * n_heads + h) * kRow + ch * kCols + cb;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = 8 * q + 4 * kh;
+          const int d = ch * kCols + cb + 8 * q + 4 * kh;  // 4 consecutive columns d .. d+3, one 8-byte store
           const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
           const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(dst + c) = make_uint2(w0, w1);
+          *reinterpret_cast<uint2*>(q_abs + q_perm_offset(r, tiles, h, d)) = make_uint2(w0, w1);
         }
       }
     }
@@ -120,7 +131,7 @@ hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const ui
   if (rows == 0) return hipSuccess;
   const int zb = (rows + kRowsPerWg - 1) / kRowsPerWg;
   if (zb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(n_heads, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, q_nope,
+  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(32 * q_tiles(n_heads), kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, q_nope,
                      q_rope, w_uk, q_abs);
   return hipGetLastError();
 }

@@ -6,25 +6,25 @@
 //                                                            concatenated parts is the sum of the parts)
 //   o_lat[h] = sum_t softmax_t(s[., h]) c_t                   (c_t serves as both key and value latent)
 //
-// Work decomposition (one work-group per (sequence, split, group of up to 128 heads)):
+// Work decomposition: one work-group of four waves per (query row, split, group of up to 128 heads).
 //   * The split's cache rows stream HBM -> LDS with buffer_load ... lds in 32-token stages (36 KB),
-//     four stage buffers deep: three stages are in flight while one is consumed. Rows past the
-//     sequence end are fetched from row 0 of the block instead, so no stale value reaches the MFMAs.
-//   * Each wave owns 32 heads. Per stage it computes S^T[token, head] = K_tile (A, from LDS) x
-//     Q^T (B, in registers) with v_mfma_f32_32x32x16_bf16 over the 576-wide row. The accumulator
+//     four stage buffers deep: three stages are in flight while one is consumed. A stage is 36 tiles
+//     of 8 rows x 128 bytes and one wave instruction moves one tile, i.e. eight whole 128-byte lines.
+//     Rows past the sequence end are fetched from row 0 of the block instead, so no stale value
+//     reaches the MFMAs.
+//   * Scores: wave w owns head tile w (32 heads) and computes S^T[token, head] = K_tile (A, from LDS)
+//     x Q^T (B, in registers) with v_mfma_f32_32x32x16_bf16 over the 576-wide row. The accumulator
 //     layout gives every lane one head and 16 tokens, so the softmax needs one cross-lane exchange
-//     (lanes l and l^32 hold the same head).
-//   * P^T goes straight from the score accumulators into the B operand of
-//     O^T[d, head] += C^T (A, ds_read_b64_tr_b16 from the same LDS stage) x P^T, all 512 latent
-//     columns accumulated in 16 32x32 fp32 tiles per wave (256 accumulator registers).
+//     (lanes l and l^32 hold the same head). The weights go to LDS as P[head][token] in bf16.
+//   * Latent reduction: wave w owns latent columns [128 w, 128 w + 128) of O^T[d, head] for every head
+//     of the group: A = C^T (ds_read_b64_tr_b16 from the stage), B = P^T (LDS). Splitting this product
+//     by columns rather than by heads reads each stage's transposed tile once instead of once per
+//     head tile (transposed reads run at half the LDS rate of plain 16-byte reads).
 //   * Online softmax against a reference max taken from the first scored stage; weights stay
 //     below 2^64 and a split whose scores climb further falls back to an exact recomputation, so
 //     the accumulators are never rescaled in the loop.
-//   * The split writes its normalised latent partial (bf16) and log-sum-exp (fp32); a separate
-//     kernel merges splits.
-//
-// LDS stage layout: chunk-major (see lds_off below), so that one DMA instruction moves two 16-byte
-// columns of all 32 rows and both operand read patterns are free of bank conflicts.
+//   * The split's normalised latent partial (bf16) is staged in LDS and written as whole 1 KB rows,
+//     its log-sum-exp (fp32) beside it; a separate kernel merges splits.
 #include "mla_internal.h"
 
 namespace mla {
@@ -37,22 +37,35 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
 
+constexpr int kWaves = 4;                           // waves per work-group
 constexpr int kStageTok = 32;                       // tokens per pipeline stage
 constexpr int kStageBytes = kStageTok * kRowBytes;  // 36864
 constexpr int kStages = 4;                          // stage buffers in LDS
-constexpr int kStageUnits = kStageBytes / 1024;     // 36 wave-wide 1 KB DMA transfers per stage
+constexpr int kBands = kRowBytes / 128;             // 9 bands of 128 bytes per cache row
+constexpr int kGroupBytes = kBands * 1024;          // 8 rows x 9 bands = 9216
+constexpr int kPHeadBytes = kStageTok * 2;          // one head's 32 bf16 weights
+constexpr int kOutPitch = kDc * 2 + 16;             // staged output row (bytes)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxExcess = 64.0f;                 // log2 units: softmax weights stay <= 2^64
 
-// LDS stage layout, chunk-major: the 16-byte chunk c (of 72) of token row r (of 32) is stored at
-//   c * 512 + (r ^ (4 * (c & 1))) * 16.
-// The score operand (32 rows at one chunk) reads 512 contiguous bytes; the transposed value operand
-// (4 rows x 2 adjacent chunks) hits two 64-byte runs that the row XOR puts in different banks.
+// LDS stage layout. Token row r (0..31) is in row group g = r / 8 at r8 = r % 8; its 16-byte chunk c
+// (0..71) is in band c / 8. Tile (g, band) is 1 KB:
+//   offset(r, c) = (9 g + c / 8) * 1024 + 128 r8 + 16 ((c % 8) ^ swz(r)),
+//   swz(r) = rot(r8) ^ 2 (g % 2),  rot(x) = ((x & 3) << 1) | (x >> 2)   (a bijection of 0..7).
+// Reads that fall in the same LDS cycle then hit distinct banks: the score operand (rows r..r+7 or
+// r..r+15 at one chunk), the transposed value operand (4 consecutive rows x 2 adjacent chunks in a
+// 16-lane group, two such groups on adjacent chunk pairs) and the 8-row copy itself (contiguous).
+__device__ __forceinline__ int rot3(int x) { return ((x & 3) << 1) | (x >> 2); }
+__device__ __forceinline__ int row_swz(int r) { return rot3(r & 7) ^ (2 * ((r >> 3) & 1)); }
+
+// P layout: head h's 32 weights at h * 64, its 8-token slot s at 16 (s ^ p_swz(h)), so that 8 or 16
+// consecutive heads reading one slot hit distinct banks.
+__device__ __forceinline__ int p_swz(int h) { return ((h >> 1) ^ (h >> 3)) & 3; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -75,38 +88,53 @@ __device__ __forceinline__ const uint16_t* block_ptr(const CacheView& c, int seq
   return c.data + phys * (int64_t)(kBlock * kRow);
 }
 
-// Start the HBM -> LDS copy of one 32-token stage (half `half` of a 64-token block): each wave
-// instruction moves chunk columns 2u and 2u+1 of all 32 rows (lane l: column 2u + l/32, row l%32);
-// rows >= valid are taken from row 0 of the block. The copy is issued from inline asm so the
-// compiler does not make later LDS reads wait for it (it would insert vmcnt(0) before reads of the
-// other stages); completion is awaited explicitly with wait_vmcnt before the barrier that publishes
-// the stage. M0 holds the LDS destination; no compiler-generated code in this kernel uses M0.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-template <int NW>
-__device__ __forceinline__ void issue_stage(const uint16_t* src_blk, int half, lds_char* dst, int valid, int wave,
-                                            int lane) {
+// Start the HBM -> LDS copy of one 32-token stage (half `half` of a 64-token block). Wave w copies row
+// group w (rows 8w..8w+7), one 1 KB tile per band: lane l fetches row 8w + l/8 at chunk
+// 8 band + ((l % 8) ^ swz(row)), which lands at tile offset 16 l = 128 r8 + 16 slot. Rows >= valid
+// are fetched from row 0 of the block. The copy is issued from inline asm so the compiler does not
+// make later LDS reads wait for it (it would insert vmcnt(0) before reads of the other stages);
+// completion is awaited explicitly with wait_vmcnt before the barrier that publishes the stage. M0
+// holds the LDS destination; no compiler-generated code in this kernel uses M0.
+struct StageCopy {
+  i32x4 rsrc;       // buffer descriptor of the block
+  uint32_t voff;    // per-lane byte offset in the block
+  uint32_t m0base;  // LDS address of this wave's row group
+  uint32_t sbase;   // byte offset of the half block
+};
+
+__device__ __forceinline__ StageCopy stage_copy(const uint16_t* src_blk, int half, uint32_t lds_stage, int valid,
+                                                int wave, int lane) {
+  StageCopy c;
   const uint64_t a = reinterpret_cast<uint64_t>(src_blk);
-  i32x4 rsrc;
-  rsrc.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  rsrc.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
-  rsrc.z = kBlock * kRowBytes;                                        // bytes addressable: the block
-  rsrc.w = 0x00020000;
-  const int odd = lane >> 5;
-  const int row = (lane & 31) ^ (4 * odd);  // logical row stored at this lane's LDS slot
-  const uint32_t voff = (uint32_t)((row < valid ? row : 0) * kRowBytes + odd * 16);
-  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + wave * 1024);
-#pragma unroll
-  for (int j = 0; j < kStageUnits / NW; ++j) {
-    const int u = j * NW + wave;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(half * kStageBytes + u * 32);
-    const uint32_t m0 = lds_base + j * NW * 1024;
+  c.rsrc.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  c.rsrc.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  c.rsrc.z = kBlock * kRowBytes;                                        // bytes addressable: the block
+  c.rsrc.w = 0x00020000;
+  const int row = 8 * wave + (lane >> 3);
+  const int chunk = (lane & 7) ^ row_swz(row);
+  c.voff = (uint32_t)((row < valid ? row : 0) * kRowBytes + chunk * 16);
+  c.m0base = __builtin_amdgcn_readfirstlane(lds_stage + wave * kGroupBytes);
+  c.sbase = __builtin_amdgcn_readfirstlane(half * kStageBytes);
+  return c;
+}
+
+// One wave instruction of a stage copy: the tile of `band`.
+__device__ __forceinline__ void stage_copy_band(const StageCopy& c, int band) {
+  const uint32_t soff = c.sbase + band * 128;
+  const uint32_t m0 = c.m0base + band * 1024;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rsrc), "s"(m0),
-                 "s"(soff)
-                 : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(c.voff), "s"(c.rsrc), "s"(m0),
+               "s"(soff)
+               : "memory", "m0");
 #pragma clang diagnostic pop
-  }
+}
+
+__device__ __forceinline__ void issue_stage(const uint16_t* src_blk, int half, uint32_t lds_stage, int valid, int wave,
+                                            int lane) {
+  const StageCopy c = stage_copy(src_blk, half, lds_stage, valid, wave, lane);
+#pragma unroll
+  for (int band = 0; band < kBands; ++band) stage_copy_band(c, band);
 }
 
 // Work-group barrier without the memory fence of __syncthreads(): that fence would also wait for
@@ -150,21 +178,28 @@ __device__ __forceinline__ int logical_block(int id, int n) {
   return xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
 }
 
+template <bool kOperandOrder>
+__device__ __forceinline__ float q_elem(const uint16_t* __restrict__ q, int tiles, int n_heads, int row, int h, int d) {
+  if constexpr (kOperandOrder) return bf16_to_f32(q[q_perm_offset(row, tiles, h, d)]);
+  return bf16_to_f32(q[((int64_t)row * n_heads + h) * kRow + d]);
+}
+
 // Exact two-pass fallback for one wave's 32 heads over tokens [t0, t1): pass 1 finds the true max,
 // pass 2 accumulates exp2(s - max) c_t in fp32. Each lane holds latent columns lane + 64k. Reads the
 // cache rows from global memory; only used when the fast path's fixed reference max is exceeded.
+template <bool kOperandOrder>
 __device__ __forceinline__ void exact_split_fallback(const CacheView& cache, int b, int qrow, int t0, int t1,
-                                                     int n_heads, int h0,
-                                                  const uint16_t* __restrict__ q_abs, float scale_log2,
-                                                  int num_splits, int s, uint16_t* __restrict__ o_partial,
-                                                  float* __restrict__ lse_partial, int lane) {
+                                                  int n_heads, int h0, const uint16_t* __restrict__ q_abs,
+                                                  float scale_log2, int num_splits, int s,
+                                                  uint16_t* __restrict__ o_partial, float* __restrict__ lse_partial,
+                                                  int lane) {
+  const int tiles = q_tiles(n_heads);
   for (int hh = 0; hh < 32; ++hh) {
     const int h = h0 + hh;
     if (h >= n_heads) break;
-    const uint16_t* qa = q_abs + ((int64_t)qrow * n_heads + h) * kRow;
     float qv[9];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) qv[k] = bf16_to_f32(qa[lane + 64 * k]);
+    for (int k = 0; k < 9; ++k) qv[k] = q_elem<kOperandOrder>(q_abs, tiles, n_heads, qrow, h, lane + 64 * k);
     float m = -INFINITY;
     for (int t = t0; t < t1; ++t) {
       const uint16_t* row = cache.data + row_offset(cache, b, t);
@@ -196,22 +231,27 @@ __device__ __forceinline__ void exact_split_fallback(const CacheView& cache, int
 
 }  // namespace
 
-template <int NW>
-__global__ void __launch_bounds__(NW * 64, 1)
-decode_mfma_kernel(CacheView cache, int n_heads, int n_head_groups, const int32_t* __restrict__ seq_lens,
+// HT: head tiles of 32 per work-group (1..4); kOperandOrder: layout of q_abs (see mla_internal.h).
+template <int HT, bool kOperandOrder>
+__global__ void __launch_bounds__(kWaves * 64, 1)
+decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __restrict__ seq_lens,
                    const int32_t* __restrict__ cu_q_lens, int batch, const uint16_t* __restrict__ q_abs,
                    float scale_log2, int split_tokens, int num_splits, uint16_t* __restrict__ o_partial,
                    float* __restrict__ lse_partial) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char p_raw[HT * 32 * kPHeadBytes];
+  __shared__ float inv_lds[HT * 32];
   __shared__ int restart_flag;
   lds_char* lds = (lds_char*)smem_raw;
+  lds_char* pl = (lds_char*)p_raw;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int kh = lane >> 5;
+  const int n = lane & 31;
   int w = logical_block(blockIdx.x, gridDim.x);
-  const int hg = w % n_head_groups;
-  w /= n_head_groups;
+  const int hg = w % n_groups;
+  w /= n_groups;
   const int s = w % num_splits;
   const int qrow = w / num_splits;  // query row: a sequence (decode) or a query token (prefill)
 
@@ -232,111 +272,200 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_head_groups, const int32_
   }
   b = __builtin_amdgcn_readfirstlane(b);
   L = __builtin_amdgcn_readfirstlane(L);
-  const int head = hg * (32 * NW) + wave * 32 + (lane & 31);
-  const bool hok = head < n_heads;
+  const int tiles_total = q_tiles(n_heads);
+  const int tiles_here = min(HT, tiles_total - 4 * hg);  // head tiles of this group (wave-uniform)
+  const int h0 = 128 * hg;                               // first head of the group
+  const bool qk_wave = wave < tiles_here;                // this wave owns head tile `wave`
+  const int head = h0 + 32 * wave + n;                   // the lane's scored head
+  const bool hok = qk_wave && head < n_heads;
   const int t0 = s * split_tokens;
   const int t1 = min(L, t0 + split_tokens);
 
   if (t1 <= t0) {  // empty split: zero partial, lse = -inf
-    const int h0 = hg * (32 * NW);
-    for (int i = threadIdx.x; i < 32 * NW * (kDc / 8); i += NW * 64) {
+    for (int i = threadIdx.x; i < 32 * HT * (kDc / 8); i += kWaves * 64) {
       const int h = h0 + i / (kDc / 8);
       if (h < n_heads)
         reinterpret_cast<uint4*>(o_partial + (((int64_t)qrow * n_heads + h) * num_splits + s) * kDc)[i % (kDc / 8)] =
             make_uint4(0, 0, 0, 0);
     }
-    if (threadIdx.x < 32 * NW && h0 + (int)threadIdx.x < n_heads)
+    if (threadIdx.x < 32 * HT && h0 + (int)threadIdx.x < n_heads)
       lse_partial[((int64_t)qrow * n_heads + h0 + threadIdx.x) * num_splits + s] = -INFINITY;
     return;
   }
 
-  // Q^T (B operand of the score MFMA): lane holds head `head`, dims 16*ks + 8*kh .. +7.
+  // Q^T (B operand of the score MFMA): lane holds head tile `wave`, head n, dims 16 ks + 8 kh .. +7.
+  // Waves without a head tile load a valid tile and never use it.
   bf16x8 qreg[36];
   {
-    const uint4* qsrc =
-        reinterpret_cast<const uint4*>(q_abs + ((int64_t)qrow * n_heads + (hok ? head : 0)) * kRow + 8 * kh);
-    // Heads past n_heads score with head 0's query: their columns are computed and dropped (no
-    // value is masked here, so nothing waits on these loads before the first copies go out).
+    const int tile = min(4 * hg + wave, tiles_total - 1);
+    if constexpr (kOperandOrder) {
+      const uint4* src = reinterpret_cast<const uint4*>(q_abs + ((int64_t)qrow * tiles_total + tile) * kQTileElems) + lane;
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, qsrc[2 * ks]);
+      for (int ks = 0; ks < 36; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, src[64 * ks]);
+    } else {
+      const int hq = min(32 * tile + n, n_heads - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(q_abs + ((int64_t)qrow * n_heads + hq) * kRow + 8 * kh);
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
+    }
   }
 
   // stage k covers tokens t0 + 32k .. +31: half (k & 1) of block blk0 + k/2 (t0 is block aligned)
   const int nstages = (t1 - t0 + kStageTok - 1) / kStageTok;
   const int blk0 = t0 / kBlock;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   if (threadIdx.x == 0) restart_flag = 0;
   // Stage 0 goes out right behind the query loads. The empty asm below reads the last query
   // register, so the compiler waits for every load here (the query, and stage 0 with it, which the
   // first step needs anyway) and knows the query is resident inside the loop; otherwise it would
-  // guard each score MFMA with a wait that also drains the copies in flight. Stages 1 and 2 follow.
-  issue_stage<NW>(block_ptr(cache, b, blk0), 0, lds, min(kStageTok, t1 - t0), wave, lane);
+  // guard each score MFMA with a wait that also drains the copies in flight. Stage 1 follows.
+  issue_stage(block_ptr(cache, b, blk0), 0, lds0, min(kStageTok, t1 - t0), wave, lane);
   asm volatile("" ::"v"(qreg[35]));
-#pragma unroll
-  for (int k = 1; k < kStages - 1; ++k)
-    if (k < nstages)
-      issue_stage<NW>(block_ptr(cache, b, blk0 + (k >> 1)), k & 1, lds + k * kStageBytes,
-                      min(kStageTok, t1 - t0 - k * kStageTok), wave, lane);
+  if (nstages > 1) issue_stage(block_ptr(cache, b, blk0), 1, lds0 + kStageBytes, min(kStageTok, t1 - t0 - kStageTok), wave, lane);
 
-  // Score operand: lane reads row (lane & 31), chunk 2*ks + kh (parity kh): one per-lane base,
-  // ks * 1024 as an immediate.
-  const uint32_t abase = kh * 512 + (((lane & 31) ^ (4 * kh)) << 4);
-  // Transposed value operand: in each 16-lane group g, lane r supplies row 16 ksp + 8 half + 4 kh + r/4
-  // and latent column 32 dblk + 16 (g&1) + 4 (r%4), i.e. chunk 4 dblk + 2 (g&1) + ((r>>1)&1) at byte
-  // 8 (r&1); only kh and that chunk parity move the row XOR: one per-lane base plus immediates.
-  const int r16 = lane & 15;
-  const int tpar = (r16 >> 1) & 1;
-  const uint32_t tbase = (2 * ((lane >> 4) & 1) + tpar) * 512 + ((4 * (kh ^ tpar)) + (r16 >> 2)) * 16 + 8 * (r16 & 1);
+  // Score operand: lane reads token row n at chunk 2 ks + kh, i.e. band ks/4 and slot
+  // (2 (ks%4) + kh) ^ swz(n) = 2 (ks%4) ^ (kh ^ swz(n)): one per-lane base per ks % 4.
+  uint32_t qk_base[4];
+  {
+    const int x = kh ^ row_swz(n);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qk_base[m] = (n >> 3) * kGroupBytes + (n & 7) * 128 + 16 * ((2 * m) ^ x);
+  }
+  // Transposed value operand (32 latent columns x 16 tokens per MFMA): in 16-lane group g, lane r
+  // supplies token 8 (g >> 1) + r/4 (+4 for the second read) of the k step and latent column
+  // 128 wave + 32 dt + 16 (g & 1) + 4 (r % 4), i.e. band 2 wave + dt/2 at chunk position
+  // 4 (dt & 1) + 2 (g & 1) + (r/2) % 2, byte 8 (r % 2). One per-lane base per (dt parity, read).
+  uint32_t pv_base[2][2];
+  {
+    const int g16 = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) {
+        const int tok = 8 * (g16 >> 1) + (r16 >> 2) + 4 * rd;
+        const int cpos = 4 * p + 2 * (g16 & 1) + ((r16 >> 1) & 1);
+        pv_base[p][rd] = (tok >> 3) * kGroupBytes + 2 * wave * 1024 + (tok & 7) * 128 + 16 * (cpos ^ row_swz(tok)) +
+                         8 * (r16 & 1);
+      }
+  }
+  // Weight operand P^T (16 tokens x 32 heads): lane reads head n of the tile, tokens 16 ksp + 8 kh .. +7.
+  uint32_t pb_base[2];
+#pragma unroll
+  for (int ksp = 0; ksp < 2; ++ksp) pb_base[ksp] = n * kPHeadBytes + 16 * ((2 * ksp + kh) ^ p_swz(n));
+  const int hl = 32 * wave + n;  // the lane's scored head within the group
 
   // Online softmax against a reference max m_ref (log2 units) fixed by the first scored stage.
   // Weights are exp2(s - m_ref) <= 2^kMaxExcess, so the accumulators are never rescaled in the loop.
   // If a later stage's max exceeds m_ref + kMaxExcess, every wave of the work-group discards its
-  // accumulators and recomputes its heads with the exact fallback below (in practice never taken).
+  // accumulators and the scoring waves recompute their heads with the exact fallback (in practice
+  // never taken).
   float m_ref = -INFINITY;
-  f32x16 o[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = f32x16{};
   float lsum = 0.f;
   bool overflow = false;
   bool restart = false;
+  f32x16 o[4 * HT];  // O^T tiles: latent columns 128 wave + 32 dt, head tile ht -> o[dt * HT + ht]
+#pragma unroll
+  for (int i = 0; i < 4 * HT; ++i) o[i] = f32x16{};
+
+  // ---- latent reduction of one stage as 8 HT MFMAs, i -> (ksp = i / (4 HT), dt = (i / HT) % 4,
+  // ht = i % HT). P^T of k step 0 is loaded by pv_begin; the register of head tile ht is reloaded
+  // with k step 1 right after its last k step 0 use (i = 3 HT + ht). The transposed C^T tile of each
+  // (ksp, dt) group is loaded one group ahead.
+  bf16x8 pb[HT];
+  i16x4 tlo, thi;
+  bf16x8 ta;
+  auto tr_load = [&](const lds_char* stp, int g) {  // g = 4 ksp + dt
+    const int off = (g >> 2) * 2 * kGroupBytes + ((g & 3) >> 1) * 1024;
+    tlo = lds_tr16(stp + pv_base[g & 1][0] + off);
+    thi = lds_tr16(stp + pv_base[g & 1][1] + off);
+  };
+  auto pv_begin = [&](const lds_char* stp) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) pb[ht] = lds_b128(pl + pb_base[0] + ht * 32 * kPHeadBytes);
+    tr_load(stp, 0);
+  };
+  auto pv_mfma = [&](const lds_char* stp, int i) {
+    const int ksp = i / (4 * HT), dt = (i / HT) % 4, ht = i % HT;
+    if (ht == 0) {
+      ta = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (i / HT + 1 < 8) tr_load(stp, i / HT + 1);
+    }
+    o[dt * HT + ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, pb[ht], o[dt * HT + ht], 0, 0, 0);
+    if (ksp == 0 && dt == 3) pb[ht] = lds_b128(pl + pb_base[1] + ht * 32 * kPHeadBytes);
+  };
+  auto pv_all = [&](const lds_char* stp) {
+    pv_begin(stp);
+#pragma unroll
+    for (int i = 0; i < 8 * HT; ++i) pv_mfma(stp, i);
+  };
+
+  // The loop is software-pipelined by one stage: step k scores stage k and, interleaved with those
+  // MFMAs and with the softmax that follows them, reduces stage k-1 with the weights P(k-1) written
+  // at the end of step k-1. Step 0 reduces a zero stage with zero weights (buffer 3 and P are
+  // cleared here), which adds nothing. Step k also copies stage k+2 into the buffer of stage k-2,
+  // one instruction every fourth score MFMA, so no wave stalls on a burst of copy instructions.
+  {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < HT * 32 * kPHeadBytes / 16; i += kWaves * 64)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(pl + 16 * i) = z;
+    for (int i = threadIdx.x; i < kStageBytes / 16; i += kWaves * 64)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (kStages - 1) * kStageBytes + 16 * i) = z;
+  }
+  constexpr int kHalfPv = 4 * HT;  // reduction MFMAs interleaved with the scores; the rest go with the softmax
+  uint32_t pw[8];
   for (int k = 0; k < nstages; ++k) {
-    // stage k has landed once only the stages issued after it (at most two) are outstanding
-    const int after = min(kStages - 2, nstages - 1 - k);
-    if (after == 2)
-      wait_vmcnt<2 * kStageUnits / NW>();
-    else if (after == 1)
-      wait_vmcnt<kStageUnits / NW>();
+    // stage k has landed once only the stage issued after it (if any) is outstanding
+    if (k + 1 < nstages)
+      wait_vmcnt<kBands>();
     else
       wait_vmcnt<0>();
-    wg_barrier();  // publishes stage k; every wave is also done with stage k-1's buffer
+    wg_barrier();  // publishes stage k and P(k-1); every wave is done with stage k-2 and P(k-2)
     restart |= restart_flag != 0;
-    if (k + kStages - 1 < nstages) {
-      const int kn = k + kStages - 1;
-      issue_stage<NW>(block_ptr(cache, b, blk0 + (kn >> 1)), kn & 1, lds + (kn % kStages) * kStageBytes,
+    const lds_char* st = lds + (k % kStages) * kStageBytes;
+    const lds_char* stp = lds + ((k + kStages - 1) % kStages) * kStageBytes;  // stage k-1
+    const bool copy_next = k + 2 < nstages;
+    StageCopy cp;
+    if (copy_next) {
+      const int kn = k + 2;
+      cp = stage_copy(block_ptr(cache, b, blk0 + (kn >> 1)), kn & 1, lds0 + (kn % kStages) * kStageBytes,
                       min(kStageTok, t1 - t0 - kn * kStageTok), wave, lane);
     }
-    const uint32_t soff = (k % kStages) * kStageBytes;
-    const int valid = min(kStageTok, t1 - t0 - k * kStageTok);
 
-    // ---- scores S^T[32 tokens x 32 heads]
+    // every wave runs this body; a wave without a head tile scores a duplicate and drops it
+    const int valid = min(kStageTok, t1 - t0 - k * kStageTok);
+    pv_begin(stp);
+    // ---- scores S^T[32 tokens x 32 heads]; half of stage k-1's reduction and the copy interleaved
     f32x16 sacc;
     {
-      const lds_char* ab = lds + (abase + soff);
-      constexpr int kAhead = 4;  // operand loads issued this many MFMAs ahead
+      constexpr int kAhead = 3;  // operand loads issued this many MFMAs ahead
       bf16x8 a_buf[kAhead];
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) a_buf[i] = lds_b128(ab + i * 1024);
+      for (int i = 0; i < kAhead; ++i) a_buf[i] = lds_b128(st + qk_base[i & 3] + (i >> 2) * 1024);
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
         const bf16x8 a = a_buf[ks % kAhead];
-        if (ks + kAhead < 36) a_buf[ks % kAhead] = lds_b128(ab + (ks + kAhead) * 1024);
+        const int kn = ks + kAhead;
+        if (kn < 36) a_buf[ks % kAhead] = lds_b128(st + qk_base[kn & 3] + (kn >> 2) * 1024);
         if (ks == 0)
           score_mfma_first(sacc, a, qreg[0]);
         else
           score_mfma(sacc, a, qreg[ks]);
+#pragma unroll
+        for (int i = ks * kHalfPv / 36; i < (ks + 1) * kHalfPv / 36; ++i) pv_mfma(stp, i);
+        if ((ks & 3) == 1 && copy_next) stage_copy_band(cp, ks >> 2);
+        // keep this order: the scheduler would otherwise hoist operand loads and run out of registers
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     score_mfma_drain(sacc);
-    // ---- softmax weights; element j is token 8*(j>>2) + 4*kh + (j&3) of the stage
+    // ---- softmax weights; element j is token 8*(j>>2) + 4*kh + (j&3) of the stage. The other half
+    // of stage k-1's reduction runs on the matrix cores meanwhile (12 slots).
+    auto pv_slot = [&](int slot) {
+#pragma unroll
+      for (int i = kHalfPv + slot * kHalfPv / 12; i < kHalfPv + (slot + 1) * kHalfPv / 12; ++i) pv_mfma(stp, i);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     if (valid < kStageTok) {  // only the split's last, partly filled stage needs a mask
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -344,13 +473,15 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_head_groups, const int32_
         if (tk >= valid) sacc[j] = -INFINITY;
       }
     }
+    pv_slot(0);
     float mx = sacc[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+    pv_slot(1);
     mx = pair_max(mx) * scale_log2;  // scale > 0: the max commutes with it
     if (m_ref == -INFINITY) m_ref = mx;
     overflow |= mx > m_ref + kMaxExcess;
-    uint32_t pw[8];
+    pv_slot(2);
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
       // raw v_exp_f32: weights below 2^-126 flush to zero, which a softmax weight can afford
@@ -358,84 +489,110 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_head_groups, const int32_
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], scale_log2, -m_ref));
       lsum += p0 + p1;
       pw[j >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+      asm volatile("" ::"v"(pw[j >> 1]));  // computed here, between the reduction MFMAs, not sunk to its store
+      pv_slot(3 + (j >> 1));
     }
-    // ---- O^T[d, head] += C^T[d, token] P^T[token, head]; transposed reads one block ahead
+    pv_slot(11);
+    if (qk_wave && __any(overflow) && lane == 0) restart_flag = 1;
+    wg_barrier();  // every wave is done with stage k-1 and P(k-1)
+    if (qk_wave) {  // P(k)[head][tokens 8 q + 4 kh .. +3] <- (pw[2q], pw[2q+1])
+      const int ps = p_swz(n);
 #pragma unroll
-    for (int ksp = 0; ksp < 2; ++ksp) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * ksp], pw[4 * ksp + 1], pw[4 * ksp + 2],
-                                                                pw[4 * ksp + 3]));
-      const lds_char* tb = lds + (tbase + soff + 16 * ksp * 16);
-      i16x4 lo = lds_tr16(tb);
-      i16x4 hi = lds_tr16(tb + 8 * 16);
-#pragma unroll
-      for (int dblk = 0; dblk < 16; ++dblk) {
-        i16x4 lo_n = lo, hi_n = hi;
-        if (dblk + 1 < 16) {
-          lo_n = lds_tr16(tb + (dblk + 1) * 2048);
-          hi_n = lds_tr16(tb + (dblk + 1) * 2048 + 8 * 16);
-        }
-        const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dblk], 0, 0, 0);
-        lo = lo_n;
-        hi = hi_n;
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(pl + hl * kPHeadBytes + 16 * (q ^ ps) + 8 * kh) =
+            u32x2{pw[2 * q], pw[2 * q + 1]};
     }
-    if (__any(overflow) && lane == 0) restart_flag = 1;
   }
-  wg_barrier();
+  wg_barrier();  // publishes P of the last stage
+  pv_all(lds + ((nstages - 1) % kStages) * kStageBytes);
+  wg_barrier();  // every wave is done with the stages and P
   restart |= restart_flag != 0;
 
   if (restart) {
-    exact_split_fallback(cache, b, qrow, t0, t1, n_heads, hg * (32 * NW) + wave * 32, q_abs, scale_log2,
-                         num_splits, s, o_partial, lse_partial, lane);
+    if (qk_wave)
+      exact_split_fallback<kOperandOrder>(cache, b, qrow, t0, t1, n_heads, h0 + 32 * wave, q_abs, scale_log2,
+                                          num_splits, s, o_partial, lse_partial, lane);
     return;
   }
 
-  lsum += __shfl_xor(lsum, 32);
-  if (!hok) return;
-  const float inv = 1.f / lsum;
-  const int64_t prow = ((int64_t)qrow * n_heads + head) * num_splits + s;
-  uint16_t* dst = o_partial + prow * kDc;
-#pragma unroll
-  for (int dblk = 0; dblk < 16; ++dblk) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 32 * dblk + 8 * g + 4 * kh;
-      const f32x2 v01 = {o[dblk][4 * g] * inv, o[dblk][4 * g + 1] * inv};
-      const f32x2 v23 = {o[dblk][4 * g + 2] * inv, o[dblk][4 * g + 3] * inv};
-      *reinterpret_cast<uint2*>(dst + d) =
-          make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2)),
-                     __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2)));
+  if (qk_wave) {
+    lsum += __shfl_xor(lsum, 32);
+    if (kh == 0) {
+      inv_lds[hl] = 1.f / lsum;
+      if (hok) lse_partial[((int64_t)qrow * n_heads + head) * num_splits + s] = (m_ref + __log2f(lsum)) * kLn2;
     }
   }
-  if (kh == 0) lse_partial[prow] = (m_ref + __log2f(lsum)) * kLn2;
+  wg_barrier();  // publishes 1/lsum of every head
+
+  // Scale by 1/lsum and stage as bf16 rows: element j of o[dt * HT + ht] is head 32 ht + n, latent
+  // column 128 wave + 32 dt + 8 (j >> 2) + 4 kh + (j & 3).
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const float iv = inv_lds[32 * ht + n];
+    char* orow = smem_raw + (32 * ht + n) * kOutPitch + 2 * (128 * wave + 4 * kh);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x2 v01 = {o[dt * HT + ht][4 * q] * iv, o[dt * HT + ht][4 * q + 1] * iv};
+        const f32x2 v23 = {o[dt * HT + ht][4 * q + 2] * iv, o[dt * HT + ht][4 * q + 3] * iv};
+        *reinterpret_cast<uint2*>(orow + 2 * (32 * dt + 8 * q)) =
+            make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2)));
+      }
+    }
+  }
+  wg_barrier();
+  // whole 1 KB rows out: wave w writes the group's heads w, w + 4, ...
+#pragma unroll 4
+  for (int i = 0; i < 8 * HT; ++i) {
+    const int r = 4 * i + wave;
+    if (r < 32 * tiles_here && h0 + r < n_heads) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem_raw + r * kOutPitch + 16 * lane);
+      reinterpret_cast<uint4*>(o_partial + (((int64_t)qrow * n_heads + h0 + r) * num_splits + s) * kDc)[lane] = v;
+    }
+  }
 }
 
-template <int NW>
-static hipError_t launch_nw(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
+template <int HT, bool kOperandOrder>
+static hipError_t launch_ht(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
                             const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, float scale, int split_tokens,
                             int num_splits, uint16_t* o_partial, float* lse_partial, hipStream_t stream) {
-  const int groups = (n_heads + 32 * NW - 1) / (32 * NW);
+  const int groups = (q_tiles(n_heads) + 3) / 4;
   const int64_t nwg = (int64_t)groups * num_splits * rows;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_mfma_kernel<NW>, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, cache, n_heads, groups,
-                     seq_lens, cu_q_lens, batch, q_abs, scale * kLog2e, split_tokens, num_splits, o_partial,
-                     lse_partial);
+  hipLaunchKernelGGL((decode_mfma_kernel<HT, kOperandOrder>), dim3((unsigned)nwg), dim3(kWaves * 64), 0, stream, cache,
+                     n_heads, groups, seq_lens, cu_q_lens, batch, q_abs, scale * kLog2e, split_tokens, num_splits,
+                     o_partial, lse_partial);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
-                            const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, float scale, int split_tokens,
-                            int num_splits, uint16_t* o_partial, float* lse_partial, hipStream_t stream) {
-  if (rows == 0) return hipSuccess;
-#define MLA_LAUNCH(NW_)                                                                                         \
-  return launch_nw<NW_>(cache, rows, n_heads, seq_lens, cu_q_lens, batch, q_abs, scale, split_tokens, num_splits, \
-                        o_partial, lse_partial, stream)
-  if (n_heads >= 128) MLA_LAUNCH(4);
-  if (n_heads > 64) MLA_LAUNCH(3);
-  if (n_heads > 32) MLA_LAUNCH(2);
+template <bool kOperandOrder>
+static hipError_t launch_layout(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
+                                const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, float scale,
+                                int split_tokens, int num_splits, uint16_t* o_partial, float* lse_partial,
+                                hipStream_t stream) {
+#define MLA_LAUNCH(HT_)                                                                                       \
+  return launch_ht<HT_, kOperandOrder>(cache, rows, n_heads, seq_lens, cu_q_lens, batch, q_abs, scale,         \
+                                       split_tokens, num_splits, o_partial, lse_partial, stream)
+  const int tiles = q_tiles(n_heads);
+  if (tiles >= 4) MLA_LAUNCH(4);
+  if (tiles == 3) MLA_LAUNCH(3);
+  if (tiles == 2) MLA_LAUNCH(2);
   MLA_LAUNCH(1);
 #undef MLA_LAUNCH
+}
+
+hipError_t launch_attention(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
+                            const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, bool q_operand_order,
+                            float scale, int split_tokens, int num_splits, uint16_t* o_partial, float* lse_partial,
+                            hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (q_operand_order)
+    return launch_layout<true>(cache, rows, n_heads, seq_lens, cu_q_lens, batch, q_abs, scale, split_tokens,
+                               num_splits, o_partial, lse_partial, stream);
+  return launch_layout<false>(cache, rows, n_heads, seq_lens, cu_q_lens, batch, q_abs, scale, split_tokens,
+                              num_splits, o_partial, lse_partial, stream);
 }
 
 }  // namespace mla

@@ -50,7 +50,7 @@ PrefillWorkspace prefill_layout(const mla_dims* d, int32_t total_q) {
   PrefillWorkspace w;
   size_t rows = (size_t)(total_q > 0 ? total_q : 0) * (size_t)d->n_heads;
   w.q_abs = 0;
-  w.o_lat = align256(rows * mla::kRow * 2);
+  w.o_lat = align256((size_t)(total_q > 0 ? total_q : 0) * mla::q_tiles(d->n_heads) * mla::kQTileElems * 2);
   w.lse = w.o_lat + align256(rows * mla::kDc * 2);
   w.total = w.lse + align256(rows * 4);
   return w;
@@ -107,7 +107,7 @@ int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, in
 
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch) {
   if (check_dims(dims) != MLA_OK || batch < 0) return 0;
-  return align256((size_t)batch * dims->n_heads * mla::kRow * 2);
+  return align256((size_t)batch * mla::q_tiles(dims->n_heads) * mla::kQTileElems * 2);
 }
 
 int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
@@ -125,7 +125,7 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   uint16_t* q_abs = static_cast<uint16_t*>(workspace);
   hipError_t e = mla::launch_absorb(batch, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
-  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs,
+  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs, true,
                                         dims->scale, split_tokens, num_splits, o_partial, lse_partial, stream));
 }
 
@@ -138,7 +138,7 @@ int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t ba
   if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
   if (batch == 0) return MLA_OK;
   if (!seq_lens || !q_abs || !o_partial || !lse_partial) return MLA_ERR_NULL;
-  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs,
+  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs, false,
                                         dims->scale, split_tokens, num_splits, o_partial, lse_partial, stream));
 }
 
@@ -181,7 +181,7 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
   // one query token per row; the whole causal key range of a row is one split (split_tokens is
   // only the split length, so any multiple of the block covering the longest sequence works)
   (void)max_q_len;
-  e = mla::launch_attention(view(cache), total_q, dims->n_heads, seq_lens, cu_q_lens, batch, q_abs, dims->scale,
+  e = mla::launch_attention(view(cache), total_q, dims->n_heads, seq_lens, cu_q_lens, batch, q_abs, true, dims->scale,
                             kMaxSplitTokens, 1, o_lat, lse, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   return launched(mla::launch_combine(total_q, dims->n_heads, 1, o_lat, lse, w_uv, out, lse_out, stream));

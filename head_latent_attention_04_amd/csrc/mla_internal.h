@@ -49,23 +49,39 @@ __device__ __forceinline__ int64_t row_offset(const CacheView& c, int seq, int p
   return (phys * kBlock + (pos % kBlock)) * (int64_t)kRow;
 }
 
+// ---- absorbed-query layout between the absorb and attention kernels ------------------------------
+// Heads are grouped in tiles of 32 (the last tile padded with zero queries). Within (row, tile) the
+// 576 elements are stored in the order the score MFMA consumes them: element (h, d) sits at
+//   [d / 16][32 * ((d / 8) % 2) + h % 32][d % 8],
+// so operand step d/16 of a whole wave is one contiguous 1 KB load (lane = 32 * half + head).
+constexpr int kQTileElems = 32 * kRow;  // 18432 elements = 36 KB per (row, head tile)
+
+__host__ __device__ inline int q_tiles(int n_heads) { return (n_heads + 31) / 32; }
+
+__host__ __device__ inline int64_t q_perm_offset(int64_t row, int tiles, int h, int d) {
+  return ((row * tiles + (h >> 5)) * (kRow / 16) + (d >> 4)) * 512 + ((((d >> 3) & 1) << 5) + (h & 31)) * 8 + (d & 7);
+}
+
 // ---- launchers (each returns the launch status) ---------------------------------------------------
 hipError_t launch_rope_append(const CacheView& cache, int n_heads, int num_tokens, const int32_t* token_seq,
                               const int32_t* token_pos, const uint16_t* c_kv, const uint16_t* k_rope,
                               uint16_t* q_rope, float theta, hipStream_t stream);
 
-// q_abs[r, h, 0:512] = W_UK[h]^T q_nope[r, h]; q_abs[r, h, 512:576] = q_rope[r, h] (bf16), r < rows.
+// q_abs(r, h, 0:512) = W_UK[h]^T q_nope[r, h]; q_abs(r, h, 512:576) = q_rope[r, h] (bf16), r < rows,
+// written in the operand-order layout above (padding heads zero).
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
                          const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream);
 
 // Split-KV attention over the latent cache with bf16 MFMA. Row r of the work is one query token:
 // decode (cu_q_lens == nullptr): row r is sequence r and sees its seq_lens[r] tokens; prefill: row j
 // is query token j (sequence located through cu_q_lens[0..batch]) and sees tokens 0..its position.
+// q_abs is in the operand-order layout (q_operand_order) or plain [rows, n_heads, 576].
 // Writes per (row, head, split) the normalised latent partial (bf16, [rows, n_heads, splits, 512])
 // and its log-sum-exp (fp32, natural log).
 hipError_t launch_attention(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
-                            const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, float scale, int split_tokens,
-                            int num_splits, uint16_t* o_partial, float* lse_partial, hipStream_t stream);
+                            const int32_t* cu_q_lens, int batch, const uint16_t* q_abs, bool q_operand_order,
+                            float scale, int split_tokens, int num_splits, uint16_t* o_partial, float* lse_partial,
+                            hipStream_t stream);
 
 // LSE merge over splits + W_UV up-projection.
 hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t* o_partial,
