@@ -5,8 +5,10 @@ Workload: decode B=32, n_h=128, d_c=512, d_R=64, d_nope=128, d_v=128, context 40
 contiguous bf16 latent cache (576 elements per token), synthetic seeded inputs with the shapes of
 the DeepSeek-V2 dimensions. One step = the whole decode hot path on one batch:
   mla_rope_append (the 32 new tokens: rotate k_R and q_R, write the rows)
-  -> mla_decode (q absorption through W_UK + split-KV attention over the latent cache)
+  -> mla_absorb (q absorption through W_UK)
+  -> mla_decode_attend (split-KV attention over the latent cache)
   -> mla_decode_combine (log-sum-exp merge of the splits + W_UV up-projection).
+(mla_absorb + mla_decode_attend is exactly mla_decode.)
 Inputs are resident in HBM before timing starts. Several independent copies of the inputs are
 rotated so that the 256 MB Infinity Cache cannot hold one step's working set.
 
@@ -68,6 +70,19 @@ def time_loop(torch, fn, n):
     e1.record(s)
     e1.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def time_each(torch, fn, n):
+    """Average duration of one launch: a pair of events on the launch stream brackets every call, so
+    the gaps between launches are not counted (what a kernel trace reports per dispatch)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(s)
+        fn(i)
+        ev[i][1].record(s)
+    ev[-1][1].synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / n
 
 
 def cpu_baseline(case, budget_s):
@@ -141,42 +156,41 @@ def main():
     torch.cuda.synchronize()
     nsets = len(sets)
 
-    def step(i):
+    def absorb(i):
         ds = sets[i % nsets]
-        ds.append_new(reset_q=False)   # the rotation repeats on the already-rotated query: same work
-        ds.decode(st, ns)
+        lib.absorb(ds.dims, ds.q_nope, ds.q_rope, ds.w_uk, ds._ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ms_step = time_loop(torch, step, args.steps)
-
-    # the dominant kernel alone: split-KV attention over the latent cache (absorbed queries ready)
-    for ds in sets:
-        ds.decode(st, ns, combine=False)
-    torch.cuda.synchronize()
-    qabs = [ds._ws[: B * H * 576 * 2].view(torch.int16) for ds in sets]
-
-    def attn(i):
+    def attend(i):
         ds = sets[i % nsets]
         o_part, lse_part = ds.partials
-        lib.decode_absorbed(ds.dims, ds.cache, ds.seq_lens, qabs[i % nsets], st, ns, o_part, lse_part)
-
-    for i in range(args.warmup):
-        attn(i)
-    ms_attn = time_loop(torch, attn, args.steps)
+        lib.decode_attend(ds.dims, ds.cache, ds.seq_lens, ds._ws, st, ns, o_part, lse_part)
 
     def comb(i):
         ds = sets[i % nsets]
         o_part, lse_part = ds.partials
         lib.decode_combine(ds.dims, B, ns, o_part, lse_part, ds.w_uv, ds.out, ds.lse)
 
-    ms_comb = time_loop(torch, comb, args.steps)
-
     def rope(i):
-        sets[i % nsets].append_new(reset_q=False)
+        sets[i % nsets].append_new(reset_q=False)  # the rotation repeats on the rotated query: same work
 
-    ms_rope = time_loop(torch, rope, args.steps)
+    def step(i):
+        rope(i)
+        absorb(i)
+        attend(i)
+        comb(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = time_loop(torch, step, args.steps)
+
+    # each kernel of the step alone, per launch (the absorbed queries of every set are in place)
+    ms = {}
+    for name, fn in (("rope_append", rope), ("absorb", absorb), ("decode_attention", attend), ("combine_wuv", comb)):
+        for i in range(args.warmup):
+            fn(i)
+        ms[name] = time_each(torch, fn, args.steps)
+    ms_attn = ms["decode_attention"]
 
     tokens = int(case.seq_lens.sum())
     flops = sum(step_flops_one_seq(case, b) for b in range(B))
@@ -207,9 +221,8 @@ def main():
         "latent_kv_GBps": round(cache_bytes / (ms_step * 1e-3) / 1e9, 1),
         "total_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_roofline_frac_hbm": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "kernels_ms": {"rope_append": round(ms_rope, 5), "decode_attention": round(ms_attn, 5),
-                       "combine_wuv": round(ms_comb, 5)},
-        "roofline": {"kernel": "decode_mfma_kernel<4> (split-KV attention)", "bound": "hbm",
+        "kernels_ms": {k: round(v, 5) for k, v in ms.items()},
+        "roofline": {"kernel": "decode_mfma_kernel<4, true> (split-KV attention, mla_decode_attend)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": cache_bytes,

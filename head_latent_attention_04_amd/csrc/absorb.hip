@@ -56,6 +56,16 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
     return;
   }
 
+  // The query rows of this work-group's first block of 32 are loaded up front with W_UK, so both
+  // latencies overlap. B operand: q_nope[r][h][16 ks + 8 kh .. +7], r = rbase + (lane & 31).
+  bf16x8 qb[8];
+  auto load_q = [&](int r0) {
+    const int r = r0 + (lane & 31);
+    const uint4* qsrc = reinterpret_cast<const uint4*>(q_nope + ((int64_t)min(r, rows - 1) * n_heads + h) * kDnope);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qsrc[2 * ks + kh]);
+  };
+  load_q(rbase);
   // stage W_UK[h][:, ch*256 : ch*256 + 256]
   const uint16_t* wsrc = w_uk + (int64_t)h * kDnope * kDc + ch * kCols;
   {
@@ -91,16 +101,8 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
   for (int rb = 0; rb < kRowsPerWg; rb += 32) {
     const int r0 = rbase + rb;
     if (r0 >= rows) break;
-    // B operand: q_nope[r][h][16 ks + 8 kh .. +7], r = r0 + (lane & 31)
-    const int r = r0 + (lane & 31);
-    bf16x8 qb[8];
-    const uint4* qsrc = reinterpret_cast<const uint4*>(q_nope + ((int64_t)min(r, rows - 1) * n_heads + h) * kDnope);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 v = qsrc[2 * ks + kh];
-      if (r >= rows) v = make_uint4(0, 0, 0, 0);
-      qb[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    const int r = r0 + (lane & 31);  // rows past the end compute from the last row and are not stored
+    if (rb > 0) load_q(r0);
 #pragma unroll
     for (int cbi = 0; cbi < 2; ++cbi) {
       const int cb = (wave * 2 + cbi) * 32;  // column block within the half

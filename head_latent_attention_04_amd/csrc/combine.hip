@@ -7,7 +7,8 @@
 // section 四: the W_UV up-projection or its absorbed equivalent).
 //
 // One work-group per (head, 16 sequences), 4 waves:
-//   1. merge: wave w merges latent columns [128 w, 128 w + 128) for the 16 sequences (fp32) and
+//   0. each wave loads its 32 rows of W_UV[h] into registers first (latency overlaps step 1);
+//   1. merge: thread t merges latent columns [32 (t % 16), +32) of sequence t / 16 (fp32) and
 //      stores them in LDS as a bf16 pair hi + lo (hi = bf16(o), lo = bf16(o - hi)), which carries
 //      the merged latent to the MFMA with about 16 significant bits;
 //   2. up-projection with bf16 MFMA: out^T[v, b] = W_UV[h][v, :] . o_lat[b, :] for the wave's 32
@@ -36,28 +37,38 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kRowsPerWg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
-  const int b = b0 + (lane & 31);
-  const bool bok = (lane & 31) < kRowsPerWg && b < batch;
 
-  // ---- 1. merge the splits of (b, h): lane owns latent columns 128 wave + 64 kh + [0, 64)
+  // W_UV rows of the up-projection (A operand: row v = 32 wave + lane % 32, columns 16 ks + 8 kh ..
+  // +7), loaded first so their latency overlaps the merge.
+  bf16x8 wa[kDc / 16];
   {
+    const uint4* wrow = reinterpret_cast<const uint4*>(w_uv + ((int64_t)h * kDv + 32 * wave + (lane & 31)) * kDc + 8 * kh);
+#pragma unroll
+    for (int ks = 0; ks < kDc / 16; ++ks) wa[ks] = __builtin_bit_cast(bf16x8, wrow[2 * ks]);
+  }
+
+  // ---- 1. merge the splits: thread t owns sequence b0 + t / 16 and latent columns 32 (t % 16) .. +31
+  {
+    const int bl = tid >> 4;
+    const int b = b0 + bl;
+    const bool bok = b < batch;
+    const int c0 = 32 * (tid & 15);
     const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
     float m = -INFINITY;
     for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
     float z = 0.f;
     if (m != -INFINITY)
       for (int s = 0; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
-    if (wave == 0 && kh == 0 && bok && lse_out)
+    if ((tid & 15) == 0 && bok && lse_out)
       lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
     const float inv_z = (m == -INFINITY) ? 0.f : 1.f / z;
-    const int c0 = 128 * wave + 64 * kh;
-    float acc[64];
+    float acc[32];
 #pragma unroll
-    for (int k = 0; k < 64; ++k) acc[k] = 0.f;
+    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
     if (bok && m != -INFINITY) {
       // splits four at a time, every load of a group issued before the first multiply-add
       for (int s0 = 0; s0 < num_splits; s0 += 4) {
-        uint4 v[4][8];
+        uint4 v[4][4];
         float wgt[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -66,13 +77,13 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
           wgt[q] = ls == -INFINITY ? 0.f : __expf(ls - m) * inv_z;
           const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(s, num_splits - 1)) * kDc + c0);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) v[q][k] = src[k];
+          for (int k = 0; k < 4; ++k) v[q][k] = src[k];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (wgt[q] == 0.f) continue;  // empty split (or past the end): contributes nothing
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
+          for (int k = 0; k < 4; ++k) {
             const uint32_t wv[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -83,10 +94,10 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
         }
       }
     }
-    char* hrow = hi_lds + (lane & 31) * kPitch + c0 * 2;
-    char* lrow = lo_lds + (lane & 31) * kPitch + c0 * 2;
+    char* hrow = hi_lds + bl * kPitch + c0 * 2;
+    char* lrow = lo_lds + bl * kPitch + c0 * 2;
 #pragma unroll
-    for (int k = 0; k < 64; k += 8) {
+    for (int k = 0; k < 32; k += 8) {
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -99,22 +110,30 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
       *reinterpret_cast<uint4*>(hrow + k * 2) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *reinterpret_cast<uint4*>(lrow + k * 2) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
+    // MFMA columns 16..31 (no sequence) read zero rows
+    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2 + 16) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2 + 32) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2 + 48) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2 + 16) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2 + 32) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2 + 48) = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
-  // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32): A = W_UV rows (global), B = merged latent (LDS)
-  const int v = 32 * wave + (lane & 31);
-  const uint4* wrow = reinterpret_cast<const uint4*>(w_uv + ((int64_t)h * kDv + v) * kDc + 8 * kh);
+  // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32): A = W_UV rows (registers), B = merged latent (LDS)
+  const int b = b0 + (lane & 31);
+  const bool bok = (lane & 31) < kRowsPerWg && b < batch;
   const lds_char* hb = (lds_char*)hi_lds + (lane & 31) * kPitch + 16 * kh;
   const lds_char* lb = (lds_char*)lo_lds + (lane & 31) * kPitch + 16 * kh;
   f32x16 acc = f32x16{};
-#pragma unroll 8
+#pragma unroll
   for (int ks = 0; ks < kDc / 16; ++ks) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, wrow[2 * ks]);
     const bf16x8 bh = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(hb + 32 * ks);
     const bf16x8 bl = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lb + 32 * ks);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bl, acc, 0, 0, 0);
   }
   // D: lane holds sequence b (column) and output dims 32 wave + 8 q + 4 kh + (0..3)
   if (bok) {

@@ -110,6 +110,35 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch) {
   return align256((size_t)batch * mla::q_tiles(dims->n_heads) * mla::kQTileElems * 2);
 }
 
+int mla_absorb(const mla_dims* dims, int32_t rows, const uint16_t* q_nope, const uint16_t* q_rope,
+               const uint16_t* w_uk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (rows < 0 || rows > 65535 * 128) return MLA_ERR_BAD_ARG;
+  if (rows == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !w_uk || !workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < mla_decode_workspace_size(dims, rows)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_absorb(rows, dims->n_heads, q_nope, q_rope, w_uk, static_cast<uint16_t*>(workspace),
+                                     stream));
+}
+
+int mla_decode_attend(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                      const void* workspace, size_t workspace_bytes, int32_t split_tokens, int32_t num_splits,
+                      uint16_t* o_partial, float* lse_partial, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!seq_lens || !workspace || !o_partial || !lse_partial) return MLA_ERR_NULL;
+  if (workspace_bytes < mla_decode_workspace_size(dims, batch)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch,
+                                        static_cast<const uint16_t*>(workspace), true, dims->scale, split_tokens,
+                                        num_splits, o_partial, lse_partial, stream));
+}
+
 int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
                const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int32_t split_tokens,
                int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* o_partial, float* lse_partial,
@@ -122,11 +151,10 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   if (!seq_lens || !q_nope || !q_rope || !w_uk || !workspace || !o_partial || !lse_partial) return MLA_ERR_NULL;
   if (workspace_bytes < mla_decode_workspace_size(dims, batch)) return MLA_ERR_BAD_ARG;
   if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
-  uint16_t* q_abs = static_cast<uint16_t*>(workspace);
-  hipError_t e = mla::launch_absorb(batch, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
-  if (e != hipSuccess) return MLA_ERR_LAUNCH;
-  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs, true,
-                                        dims->scale, split_tokens, num_splits, o_partial, lse_partial, stream));
+  st = mla_absorb(dims, batch, q_nope, q_rope, w_uk, workspace, workspace_bytes, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_attend(dims, cache, batch, seq_lens, workspace, workspace_bytes, split_tokens, num_splits,
+                           o_partial, lse_partial, stream);
 }
 
 int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,

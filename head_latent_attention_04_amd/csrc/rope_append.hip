@@ -20,6 +20,22 @@ __global__ void __launch_bounds__(256) rope_append_kernel(CacheView cache, int n
                                                            uint16_t* __restrict__ q_rope, double log2_theta) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
+
+  // Every load of this token is issued before the first store (the query is rotated in place, so a
+  // load after a store of the same array would wait for it), and the token's inputs before its
+  // position, which only the angles and the destination row depend on.
+  constexpr int kQPerThread = 16;  // n_heads * 32 pairs / 256 threads, for up to 128 heads per pass
+  uint32_t* q = q_rope != nullptr ? reinterpret_cast<uint32_t*>(q_rope + (int64_t)i * n_heads * kDr) : nullptr;
+  const int nq = n_heads * (kDr / 2);
+  uint4 ckv = make_uint4(0, 0, 0, 0);
+  if (tid < kDc / 8) ckv = reinterpret_cast<const uint4*>(c_kv + (int64_t)i * kDc)[tid];
+  uint32_t kr = 0;
+  if (tid < kDr / 2) kr = reinterpret_cast<const uint32_t*>(k_rope + (int64_t)i * kDr)[tid];
+  uint32_t v0[kQPerThread];  // first pass of the query pairs
+  if (q != nullptr) {
+#pragma unroll
+    for (int k = 0; k < kQPerThread; ++k) v0[k] = tid + 256 * k < nq ? q[tid + 256 * k] : 0u;
+  }
   const int seq = token_seq[i];
   const int pos = token_pos[i];
   uint16_t* row = cache.data + row_offset(cache, seq, pos);
@@ -34,27 +50,31 @@ __global__ void __launch_bounds__(256) rope_append_kernel(CacheView cache, int n
     s_cos[tid] = c;
     s_sin[tid] = s;
   }
-  // c_KV: 512 bf16 = 64 x 16 bytes, copied unchanged
-  if (tid < kDc / 8) {
-    reinterpret_cast<uint4*>(row)[tid] = reinterpret_cast<const uint4*>(c_kv + (int64_t)i * kDc)[tid];
-  }
   __syncthreads();
-  if (tid >= 64 && tid < 64 + kDr / 2) {
-    int j = tid - 64;
-    const uint16_t* k = k_rope + (int64_t)i * kDr;
-    double x0 = bf16_to_f32(k[2 * j]), x1 = bf16_to_f32(k[2 * j + 1]);
-    double c = s_cos[j], s = s_sin[j];
-    uint32_t packed = (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
-    reinterpret_cast<uint32_t*>(row + kDc)[j] = packed;
+  // c_KV: 512 bf16 = 64 x 16 bytes, copied unchanged; k_R pair j rotated by angle j
+  if (tid < kDc / 8) reinterpret_cast<uint4*>(row)[tid] = ckv;
+  if (tid < kDr / 2) {
+    const double x0 = bf16_to_f32((uint16_t)(kr & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(kr >> 16));
+    const double c = s_cos[tid], s = s_sin[tid];
+    reinterpret_cast<uint32_t*>(row + kDc)[tid] =
+        (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
   }
-  if (q_rope != nullptr) {
-    uint32_t* q = reinterpret_cast<uint32_t*>(q_rope + (int64_t)i * n_heads * kDr);
-    for (int p = tid; p < n_heads * (kDr / 2); p += blockDim.x) {
-      int j = p % (kDr / 2);
-      uint32_t v = q[p];
-      double x0 = bf16_to_f32((uint16_t)(v & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(v >> 16));
-      double c = s_cos[j], s = s_sin[j];
-      q[p] = (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
+  if (q != nullptr) {
+    // pair p = tid + 256 k of the token's [n_heads, 32] pairs; its angle index is p % 32 = tid % 32
+    const double c = s_cos[tid % (kDr / 2)], s = s_sin[tid % (kDr / 2)];
+    for (int base = 0; base < nq; base += 256 * kQPerThread) {
+      uint32_t v[kQPerThread];
+#pragma unroll
+      for (int k = 0; k < kQPerThread; ++k) {
+        const int p = base + tid + 256 * k;
+        v[k] = base == 0 ? v0[k] : (p < nq ? q[p] : 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < kQPerThread; ++k) {
+        const int p = base + tid + 256 * k;
+        const double x0 = bf16_to_f32((uint16_t)(v[k] & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(v[k] >> 16));
+        if (p < nq) q[p] = (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
+      }
     }
   }
 }

@@ -49,6 +49,9 @@ EXPORTS = {
     "mla_decode_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp, _i32,
                                   _i32, _vp, _sz, _vp, _vp, _vp]),
+    "mla_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_decode_attend": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _sz, _i32,
+                                         _i32, _vp, _vp, _vp]),
     "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
                                            _i32, _vp, _vp, _vp]),
     "mla_decode_combine": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -157,6 +160,28 @@ def decode(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split
         _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
     _check("mla_decode", st)
+
+
+def absorb(dims: MlaDims, q_nope, q_rope, w_uk, workspace, stream=None):
+    R = q_nope.shape[0]
+    H = dims.n_heads
+    st = load().mla_absorb(
+        ctypes.byref(dims), R, _ptr(q_nope, "q_nope", BF16, R * H * dims.d_nope),
+        _ptr(q_rope, "q_rope", BF16, R * H * dims.d_rope), _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mla_absorb", st)
+
+
+def decode_attend(dims: MlaDims, cache: MlaCache, seq_lens, workspace, split_tokens: int, num_splits: int, o_partial,
+                  lse_partial, stream=None):
+    B = seq_lens.numel()
+    H = dims.n_heads
+    st = load().mla_decode_attend(
+        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), split_tokens, num_splits,
+        _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
+        _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
+    _check("mla_decode_attend", st)
 
 
 def decode_absorbed(dims: MlaDims, cache: MlaCache, seq_lens, q_abs, split_tokens: int, num_splits: int, o_partial,

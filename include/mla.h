@@ -134,6 +134,25 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
                uint16_t* o_partial, float* lse_partial, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mla_absorb / mla_decode_attend - the two halves of mla_decode, for callers that schedule or time
+ * them apart ("论文复现工坊 No.4", section 4: the absorption Q W_UK^T is a step of its own before
+ * scoring against c^KV).
+ *   mla_absorb(rows): q_abs[r, h] = [W_UK[h]^T q_nope[r, h] (d_c, bf16) | q_rope[r, h]] for r < rows,
+ *     written to `workspace` in the library's internal operand order (opaque to the caller);
+ *     q_nope [rows, n_heads, d_nope], q_rope [rows, n_heads, d_rope] bf16; w_uk as for mla_decode;
+ *     workspace >= mla_decode_workspace_size(dims, rows) bytes, 256-byte aligned.
+ *   mla_decode_attend(batch): mla_decode's attention and outputs, reading the queries that
+ *     mla_absorb(rows = batch) left in `workspace` (same dims, same workspace).
+ * mla_absorb followed by mla_decode_attend on one stream computes exactly what mla_decode does.
+ * ------------------------------------------------------------------------------------------- */
+int mla_absorb(const mla_dims* dims, int32_t rows, const uint16_t* q_nope, const uint16_t* q_rope,
+               const uint16_t* w_uk, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int mla_decode_attend(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                      const void* workspace, size_t workspace_bytes, int32_t split_tokens, int32_t num_splits,
+                      uint16_t* o_partial, float* lse_partial, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mla_decode_absorbed - mla_decode for callers that already hold the absorbed queries, e.g. with
  * W_UK folded into the query up-projection ahead of time ("淺析DeepSeek多頭潛在注意力機制（MLA）",
  * "MLA的數學原理": x_t (W_q W_k^T) is one precomputable product).

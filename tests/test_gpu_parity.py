@@ -274,3 +274,25 @@ def test_decode_absorbed_entry_point():
                        case.w_uk, case.w_uv)
     assert_close(to_f64(dc.out), ref, "decode_absorbed")
     assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
+
+
+def test_absorb_then_attend_equals_decode_bitwise():
+    """mla_absorb + mla_decode_attend on one stream gives exactly mla_decode's partials."""
+    say("[decode] absorb + attend split entry points")
+    case = make_case("split_api", 83, 128, [700, 1, 64, 2100], paged=True, spare_blocks=3)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.append_new()
+    st, ns = 256, 9
+    dc.alloc_decode(ns)
+    o_part, lse_part = dc.partials
+    dc.decode(st, ns, combine=False)
+    torch.cuda.synchronize()
+    ref_o, ref_l = o_part.clone(), lse_part.clone()
+    o_part.fill_(0)
+    lse_part.fill_(0)
+    lib.absorb(dc.dims, dc.q_nope, dc.q_rope, dc.w_uk, dc._ws)
+    lib.decode_attend(dc.dims, dc.cache, dc.seq_lens, dc._ws, st, ns, o_part, lse_part)
+    torch.cuda.synchronize()
+    assert torch.equal(o_part, ref_o)
+    assert torch.equal(lse_part, ref_l)
