@@ -30,6 +30,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_04_amd", "csrc", "decode_mfma.hip")
+COPY_PROBE_BYTES = 256 << 20
 
 
 def parse():
@@ -192,6 +193,15 @@ def main():
         ms[name] = time_each(torch, fn, args.steps)
     ms_attn = ms["decode_attention"]
 
+    # a plain device copy of known size: the achievable-bandwidth context for the roofline, and the
+    # calibration kernel for the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a counter run
+    copy_bytes = COPY_PROBE_BYTES
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms_copy = time_each(torch, lambda i: dst.copy_(src), 5)
+    del src, dst
+
     tokens = int(case.seq_lens.sum())
     flops = sum(step_flops_one_seq(case, b) for b in range(B))
     cache_bytes = tokens * 1152
@@ -227,6 +237,8 @@ def main():
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": cache_bytes,
                      "mfma_tflops": round(tokens * H * (2 * 576 + 2 * 512) / (ms_attn * 1e-3) / 1e12, 1)},
+        "copy_probe": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                       "GBps": round(2 * copy_bytes / (ms_copy * 1e-3) / 1e9, 1)},
         "device": props.name,
     }
     if not args.no_cpu:
