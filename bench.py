@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -41,6 +43,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode: B=32, n_h=128, 4K context (the headline); prefill: chunked prefill, 2 x 1024 "
+                         "new tokens after 8192 cached")
     return ap.parse_args()
 
 
@@ -141,6 +146,8 @@ def main():
     torch.cuda.set_device(0)
     lib.load()
     props = torch.cuda.get_device_properties(0)
+    if args.workload == "prefill":
+        return prefill_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -243,6 +250,107 @@ def main():
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_flops(case):
+    """Algorithmic FLOP of the chunked prefill: per query at position p, (p + 1) visible keys x n_h x
+    (2 * 576 score + 2 * 512 reduction), plus absorption and up-projection per query and head."""
+    H = case.n_heads
+    pos = case.q_positions().astype(np.float64)
+    attn = float(np.sum(pos + 1.0)) * H * (2 * 576 + 2 * 512)
+    proj = float(len(pos)) * H * 2 * (128 * 512 * 2)
+    return attn, proj
+
+
+def prefill_cpu_baseline(case, budget_s):
+    """fp64 expanded-form oracle on query tokens of the same prefill (all heads), until the budget
+    is spent; rate in algorithmic TFLOP/s."""
+    from oracle import mla_oracle as O
+    from workloads import BF16_NAN
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
+    cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
+                             case.c_kv, case.k_rope)
+    pos_all = case.q_positions()
+    q_rot = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(case.q_rope), pos_all[:, None]))
+    H = case.n_heads
+    rows, flops = [], 0.0
+    t0 = time.perf_counter()
+    j = 0
+    while j < len(pos_all) and time.perf_counter() - t0 < budget_s:
+        O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.cu_q_lens, case.q_nope,
+                  q_rot, case.w_uk, case.w_uv, rows_sel=[j])
+        flops += (float(pos_all[j]) + 1.0) * H * (2 * 576 + 2 * 512) + H * 2 * (128 * 512 * 2)
+        rows.append(j)
+        j += 97  # spread the sample over both sequences and all positions
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} of {len(pos_all)} query tokens (every 97th, all {H} heads), fp64 expanded "
+                      f"form, {dt:.1f} s"}
+
+
+def prefill_main(args, torch, lib, props):
+    from head_latent_attention_04_amd.runner import DeviceCase
+    from workloads import make_config
+
+    case = make_config(4)
+    H = case.n_heads
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.prepare_step_inputs()
+    dc.append_new()
+    dc.alloc_prefill()
+    torch.cuda.synchronize()
+
+    def rope(i):
+        dc.append_new(reset_q=False)  # the rotation repeats on the rotated query: same work
+
+    def prefill(i):
+        dc.prefill()
+
+    def step(i):
+        rope(i)
+        prefill(i)
+
+    steps = max(1, min(args.steps, 20))
+    for i in range(max(1, min(args.warmup, 3))):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = time_loop(torch, step, steps)
+    ms = {"rope_append": time_each(torch, rope, steps), "chunked_prefill": time_each(torch, prefill, steps)}
+    attn, proj = prefill_flops(case)
+    total_q = int(case.cu_q_lens[-1])
+    result = {
+        "metric": "absorbed MLA chunked prefill TFLOP/s, n_h=128, 2 x 1024 new tokens after 8192 cached",
+        "value": round((attn + proj) / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(1, min(args.warmup, 3)),
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"chunked prefill B={case.batch} q_len=1024 cached=8192 n_h={H} causal, paged bf16 "
+                               f"latent cache", "total_q": total_q, "n_heads": H, "d_c": 512, "d_rope": 64,
+                   "d_nope": 128, "d_v": 128},
+        "kernels_ms": {k: round(v, 4) for k, v in ms.items()},
+        "roofline": {"kernel": "mla_chunked_prefill (absorb + decode_mfma_kernel<4, true> causal rows + combine)",
+                     "bound": "mfma", "achieved": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": attn + proj},
+        "device": props.name,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = prefill_cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

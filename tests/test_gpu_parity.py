@@ -227,6 +227,33 @@ def test_decode_configs_full_size_sampled(cfg):
     assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
 
 
+def test_prefill_config4_full_size_sampled():
+    """Chunked prefill at full size (2 sequences, 1024 new tokens after 8192 cached, 128 heads): every
+    output finite; sampled (query token, head) outputs, including the first and last query of each
+    sequence, match the oracle."""
+    say("[prefill] config 4 full size")
+    case = make_config(4)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.append_new()
+    dc.alloc_prefill()
+    dc.prefill()
+    torch.cuda.synchronize()
+    out = to_f64(dc.out)
+    lse = dc.lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(4)
+    cu = case.cu_q_lens
+    rows = sorted(set([int(cu[0]), int(cu[1]) - 1, int(cu[1]), int(cu[2]) - 1] + rng.integers(0, int(cu[-1]), 2).tolist()))
+    heads = sorted(set([0, case.n_heads - 1] + rng.integers(0, case.n_heads, 4).tolist()))
+    cache, q_rot = oracle_cache(case)
+    ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, cu, case.q_nope, q_rot,
+                        case.w_uk, case.w_uv, rows_sel=rows, heads=heads)
+    sel = np.ix_(rows, heads)
+    assert_close(out[sel], ref[sel], "config 4 sampled")
+    assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
+
+
 def test_decode_large_score_growth_uses_exact_path():
     """Scores that climb by far more than 2^64 after the first sub-tile (q_nope = 0 and the RoPE keys
     of tokens >= 64 scaled by 64, all exact in bf16): the decode still matches the oracle."""
