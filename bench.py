@@ -10,7 +10,8 @@ the DeepSeek-V2 dimensions. One step = the whole decode hot path on one batch:
   -> mla_decode_combine (log-sum-exp merge of the splits + W_UV up-projection).
 (mla_absorb + mla_decode_attend is exactly mla_decode.)
 Inputs are resident in HBM before timing starts. Several independent copies of the inputs are
-rotated so that the 256 MB Infinity Cache cannot hold one step's working set.
+rotated so that the 256 MB Infinity Cache cannot hold one step's working set. The step is timed
+as eager launches; the same four launches captured in a HIP graph and replayed are reported beside.
 
 Prints ONE JSON line. `value` is the step's algorithmic TFLOP/s; latent-KV GB/s, the dominant
 kernel's roofline fraction and the fp64 CPU oracle's rate (on the host's cores) ride along.
@@ -190,7 +191,25 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ms_step = time_loop(torch, step, args.steps)
+    ms_step_eager = time_loop(torch, step, args.steps)
+
+    # The same step as a HIP graph of the four launches (one graph per input set), replayed: reported
+    # beside the eager step (the gaps between dependent kernels stay on the device either way).
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for k in range(nsets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(k)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % nsets].replay()
+    ms_step_graph = time_loop(torch, lambda i: graphs[i % nsets].replay(), args.steps)
+    ms_step = ms_step_eager
 
     # each kernel of the step alone, per launch (the absorbed queries of every set are in place)
     ms = {}
@@ -228,6 +247,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_graph_replay": round(ms_step_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

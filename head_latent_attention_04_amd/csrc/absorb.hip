@@ -10,10 +10,12 @@
 //
 // Per head this is a small GEMM, computed transposed with bf16 MFMA:
 //   q_abs^T[c, r] = sum_d W_UK[h][d][c] q_nope[r, h, d]     (M = c, N = r, K = d)
-// One work-group per (head, half of the 512 latent columns, up to 128 rows). The 128 x 256 slice of
-// W_UK[h] is staged in LDS once (rows padded to 544 bytes so the transposed reads of 4 rows hit
+// One work-group per (head, half of the 512 latent columns, a range of 32-row blocks). The 128 x 256
+// slice of W_UK[h] is staged in LDS once (rows padded to 544 bytes so the transposed reads of 4 rows hit
 // different banks) and read with ds_read_b64_tr_b16 as the d-contiguous A operand; q_nope rows are
 // the B operand straight from global memory. fp32 accumulation, one bf16 rounding.
+#include <algorithm>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -27,28 +29,28 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kCols = 256;                 // latent columns per work-group
 constexpr int kPitch = kCols * 2 + 32;     // LDS row pitch in bytes (544)
-constexpr int kRowsPerWg = 128;            // 4 blocks of 32 rows
 
 __device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
 }  // namespace
 
-__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, const uint16_t* __restrict__ q_nope,
+__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, int rows_per_wg,
+                                                          const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           uint16_t* __restrict__ q_abs) {
   __shared__ __attribute__((aligned(16))) char w_lds[kDnope * kPitch];
   const int h = blockIdx.x;
   const int ch = blockIdx.y;                 // column half
-  const int rbase = blockIdx.z * kRowsPerWg;
+  const int rbase = blockIdx.z * rows_per_wg;  // this work-group's rows (a multiple of 32)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
   const int tiles = q_tiles(n_heads);
   lds_char* lds = (lds_char*)w_lds;
 
   if (h >= n_heads) {  // padding head of the last tile: zero query (columns of this half, RoPE part in half 0)
     const int cols = ch == 0 ? kCols + kDr : kCols;
-    for (int i = tid; i < kRowsPerWg * (cols / 8); i += 256) {
+    for (int i = tid; i < rows_per_wg * (cols / 8); i += 256) {
       const int r = rbase + i / (cols / 8), c8 = i % (cols / 8);
       const int d = c8 * 8 < kCols ? ch * kCols + c8 * 8 : kDc + (c8 * 8 - kCols);
       if (r < rows) *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, d)) = make_uint4(0, 0, 0, 0);
@@ -57,15 +59,16 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
   }
 
   // The query rows of this work-group's first block of 32 are loaded up front with W_UK, so both
-  // latencies overlap. B operand: q_nope[r][h][16 ks + 8 kh .. +7], r = rbase + (lane & 31).
-  bf16x8 qb[8];
-  auto load_q = [&](int r0) {
+  // latencies overlap; each later block's rows are loaded while the previous block computes.
+  // B operand: q_nope[r][h][16 ks + 8 kh .. +7], r = r0 + (lane & 31).
+  bf16x8 qb[8], qn[8];
+  auto load_q = [&](bf16x8* dst, int r0) {
     const int r = r0 + (lane & 31);
     const uint4* qsrc = reinterpret_cast<const uint4*>(q_nope + ((int64_t)min(r, rows - 1) * n_heads + h) * kDnope);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qsrc[2 * ks + kh]);
+    for (int ks = 0; ks < 8; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, qsrc[2 * ks + kh]);
   };
-  load_q(rbase);
+  load_q(qb, rbase);
   // stage W_UK[h][:, ch*256 : ch*256 + 256]
   const uint16_t* wsrc = w_uk + (int64_t)h * kDnope * kDc + ch * kCols;
   {
@@ -84,7 +87,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
   }
   // the RoPE part of the row is copied unchanged (column half 0 does it)
   if (ch == 0) {
-    for (int i = tid; i < kRowsPerWg * (kDr / 8); i += 256) {
+    for (int i = tid; i < rows_per_wg * (kDr / 8); i += 256) {
       const int r = rbase + i / (kDr / 8), c8 = i % (kDr / 8);
       if (r < rows)
         *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, kDc + 8 * c8)) =
@@ -98,11 +101,10 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
   const int i16 = lane & 15, g = lane >> 4;
   const uint32_t abase = ((i16 >> 2) + 8 * kh) * kPitch + (16 * (g & 1) + 4 * (i16 & 3)) * 2;
 
-  for (int rb = 0; rb < kRowsPerWg; rb += 32) {
-    const int r0 = rbase + rb;
-    if (r0 >= rows) break;
+  const int rend = min(rows, rbase + rows_per_wg);
+  for (int r0 = rbase; r0 < rend; r0 += 32) {
     const int r = r0 + (lane & 31);  // rows past the end compute from the last row and are not stored
-    if (rb > 0) load_q(r0);
+    if (r0 + 32 < rend) load_q(qn, r0 + 32);
 #pragma unroll
     for (int cbi = 0; cbi < 2; ++cbi) {
       const int cb = (wave * 2 + cbi) * 32;  // column block within the half
@@ -115,26 +117,44 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
         const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qb[ks], acc, 0, 0, 0);
       }
-      if (r < rows) {
+      // Lane (row, kh) holds columns 8 q + 4 kh .. +3 of its row. For each pair of groups (q, q+1) the
+      // lanes l and l ^ 32 trade halves so that the low lane writes group q and the high lane group
+      // q+1 as whole 16-byte pieces (8 consecutive columns, one operand-order chunk): each lane sends
+      // the half its partner is missing.
+      uint32_t w[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int d = ch * kCols + cb + 8 * q + 4 * kh;  // 4 consecutive columns d .. d+3, one 8-byte store
-          const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
-          const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(q_abs + q_perm_offset(r, tiles, h, d)) = make_uint2(w0, w1);
-        }
+      for (int q = 0; q < 4; ++q) {
+        w[2 * q] = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
+        w[2 * q + 1] = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q += 2) {
+        const uint32_t t0 = __shfl_xor(kh ? w[2 * q] : w[2 * q + 2], 32);
+        const uint32_t t1 = __shfl_xor(kh ? w[2 * q + 1] : w[2 * q + 3], 32);
+        const uint4 v = kh == 0 ? make_uint4(w[2 * q], w[2 * q + 1], t0, t1)
+                                : make_uint4(t0, t1, w[2 * q + 2], w[2 * q + 3]);
+        const int d = ch * kCols + cb + 8 * (q + kh);
+        if (r < rows) *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, d)) = v;
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = qn[ks];
   }
 }
 
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
                          const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const int zb = (rows + kRowsPerWg - 1) / kRowsPerWg;
+  // blocks of 32 rows per work-group: one for small batches, more when there are many rows, so
+  // that about 1024 work-groups each stage their W_UK slice once
+  const int hp = 32 * q_tiles(n_heads);
+  const int64_t nrb = (rows + 31) / 32;
+  const int64_t bpw = std::max<int64_t>(1, (nrb * hp * 2 + 1023) / 1024);
+  const int rows_per_wg = (int)std::min<int64_t>(32 * bpw, 32 * nrb);
+  const int zb = (rows + rows_per_wg - 1) / rows_per_wg;
   if (zb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(32 * q_tiles(n_heads), kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, q_nope,
-                     q_rope, w_uk, q_abs);
+  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, rows_per_wg,
+                     q_nope, q_rope, w_uk, q_abs);
   return hipGetLastError();
 }
 

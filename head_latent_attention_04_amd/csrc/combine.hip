@@ -6,7 +6,7 @@
 // token ("论文复现工坊 No.4", section 1; "Multi-Head Latent Attention: DeepSeek V2/V3 工程视角",
 // section 四: the W_UV up-projection or its absorbed equivalent).
 //
-// One work-group per (head, 16 sequences), 4 waves:
+// One work-group per (head, range of 16-sequence blocks), 4 waves:
 //   0. each wave loads its 32 rows of W_UV[h] into registers first (latency overlaps step 1);
 //   1. merge: thread t merges latent columns [32 (t % 16), +32) of sequence t / 16 (fp32) and
 //      stores them in LDS as a bf16 pair hi + lo (hi = bf16(o), lo = bf16(o - hi)), which carries
@@ -14,6 +14,8 @@
 //   2. up-projection with bf16 MFMA: out^T[v, b] = W_UV[h][v, :] . o_lat[b, :] for the wave's 32
 //      output columns v (M = v, N = b padded to 32 with zero rows, K = c), hi and lo accumulated
 //      into the same fp32 tile.
+#include <algorithm>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -27,7 +29,7 @@ constexpr int kRowsPerWg = 16;  // sequences per work-group (MFMA columns 16..31
 constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded (conflict-free b128 reads)
 }  // namespace
 
-__global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_heads, int num_splits,
+__global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_heads, int num_splits, int blocks_per_wg,
                                                            const uint16_t* __restrict__ o_partial,
                                                            const float* __restrict__ lse_partial,
                                                            const uint16_t* __restrict__ w_uv,
@@ -35,7 +37,6 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
   __shared__ __attribute__((aligned(16))) char hi_lds[32 * kPitch];
   __shared__ __attribute__((aligned(16))) char lo_lds[32 * kPitch];
   const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kRowsPerWg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
 
   // W_UV rows of the up-projection (A operand: row v = 32 wave + lane % 32, columns 16 ks + 8 kh ..
@@ -47,103 +48,110 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
     for (int ks = 0; ks < kDc / 16; ++ks) wa[ks] = __builtin_bit_cast(bf16x8, wrow[2 * ks]);
   }
 
-  // ---- 1. merge the splits: thread t owns sequence b0 + t / 16 and latent columns 32 (t % 16) .. +31
+  // MFMA columns 16..31 (no sequence) read zero rows (written once; the loop only rewrites rows 0..15)
   {
-    const int bl = tid >> 4;
-    const int b = b0 + bl;
-    const bool bok = b < batch;
-    const int c0 = 32 * (tid & 15);
-    const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
-    float m = -INFINITY;
-    for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
-    float z = 0.f;
-    if (m != -INFINITY)
-      for (int s = 0; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
-    if ((tid & 15) == 0 && bok && lse_out)
-      lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
-    const float inv_z = (m == -INFINITY) ? 0.f : 1.f / z;
-    float acc[32];
+    const int zr = 16 + (tid >> 4), zc = 32 * (tid & 15);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-    if (bok && m != -INFINITY) {
-      // splits four at a time, every load of a group issued before the first multiply-add
-      for (int s0 = 0; s0 < num_splits; s0 += 4) {
-        uint4 v[4][4];
-        float wgt[4];
+    for (int k = 0; k < 4; ++k) {
+      *reinterpret_cast<uint4*>(hi_lds + zr * kPitch + zc * 2 + 16 * k) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(lo_lds + zr * kPitch + zc * 2 + 16 * k) = make_uint4(0, 0, 0, 0);
+    }
+  }
+  // blocks of 16 sequences; W_UV stays in registers across them
+  const int nblk = (batch + kRowsPerWg - 1) / kRowsPerWg;
+  const int blk_end = min(nblk, (int)(blockIdx.y + 1) * blocks_per_wg);
+  for (int blk = blockIdx.y * blocks_per_wg; blk < blk_end; ++blk) {
+    const int b0 = blk * kRowsPerWg;
+    // ---- 1. merge the splits: thread t owns sequence b0 + t / 16 and latent columns 32 (t % 16) .. +31
+    {
+      const int bl = tid >> 4;
+      const int b = b0 + bl;
+      const bool bok = b < batch;
+      const int c0 = 32 * (tid & 15);
+      const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
+      float m = -INFINITY;
+      for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
+      float z = 0.f;
+      if (m != -INFINITY)
+        for (int s = 0; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
+      if ((tid & 15) == 0 && bok && lse_out)
+        lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
+      const float inv_z = (m == -INFINITY) ? 0.f : 1.f / z;
+      float acc[32];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int s = s0 + q;
-          const float ls = s < num_splits ? lse_partial[base + s] : -INFINITY;
-          wgt[q] = ls == -INFINITY ? 0.f : __expf(ls - m) * inv_z;
-          const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(s, num_splits - 1)) * kDc + c0);
+      for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+      if (bok && m != -INFINITY) {
+        // splits four at a time, every load of a group issued before the first multiply-add
+        for (int s0 = 0; s0 < num_splits; s0 += 4) {
+          uint4 v[4][4];
+          float wgt[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) v[q][k] = src[k];
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int s = s0 + q;
+            const float ls = s < num_splits ? lse_partial[base + s] : -INFINITY;
+            wgt[q] = ls == -INFINITY ? 0.f : __expf(ls - m) * inv_z;
+            const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(s, num_splits - 1)) * kDc + c0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (wgt[q] == 0.f) continue;  // empty split (or past the end): contributes nothing
+            for (int k = 0; k < 4; ++k) v[q][k] = src[k];
+          }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t wv[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
+          for (int q = 0; q < 4; ++q) {
+            if (wgt[q] == 0.f) continue;  // empty split (or past the end): contributes nothing
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[8 * k + 2 * e] = fmaf(wgt[q], __uint_as_float(wv[e] << 16), acc[8 * k + 2 * e]);
-              acc[8 * k + 2 * e + 1] = fmaf(wgt[q], __uint_as_float(wv[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t wv[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                acc[8 * k + 2 * e] = fmaf(wgt[q], __uint_as_float(wv[e] << 16), acc[8 * k + 2 * e]);
+                acc[8 * k + 2 * e + 1] = fmaf(wgt[q], __uint_as_float(wv[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+              }
             }
           }
         }
       }
-    }
-    char* hrow = hi_lds + bl * kPitch + c0 * 2;
-    char* lrow = lo_lds + bl * kPitch + c0 * 2;
+      char* hrow = hi_lds + bl * kPitch + c0 * 2;
+      char* lrow = lo_lds + bl * kPitch + c0 * 2;
 #pragma unroll
-    for (int k = 0; k < 32; k += 8) {
-      uint32_t hw[4], lw[4];
+      for (int k = 0; k < 32; k += 8) {
+        uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint16_t h0 = f32_to_bf16(acc[k + e]), h1 = f32_to_bf16(acc[k + e + 1]);
-        const uint16_t l0 = f32_to_bf16(acc[k + e] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(acc[k + e + 1] - bf16_to_f32(h1));
-        hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        for (int e = 0; e < 8; e += 2) {
+          const uint16_t h0 = f32_to_bf16(acc[k + e]), h1 = f32_to_bf16(acc[k + e + 1]);
+          const uint16_t l0 = f32_to_bf16(acc[k + e] - bf16_to_f32(h0));
+          const uint16_t l1 = f32_to_bf16(acc[k + e + 1] - bf16_to_f32(h1));
+          hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        *reinterpret_cast<uint4*>(hrow + k * 2) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(lrow + k * 2) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
-      *reinterpret_cast<uint4*>(hrow + k * 2) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(lrow + k * 2) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
-    // MFMA columns 16..31 (no sequence) read zero rows
-    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2 + 16) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2 + 32) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(hi_lds + (16 + bl) * kPitch + c0 * 2 + 48) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2 + 16) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2 + 32) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lo_lds + (16 + bl) * kPitch + c0 * 2 + 48) = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32): A = W_UV rows (registers), B = merged latent (LDS)
-  const int b = b0 + (lane & 31);
-  const bool bok = (lane & 31) < kRowsPerWg && b < batch;
-  const lds_char* hb = (lds_char*)hi_lds + (lane & 31) * kPitch + 16 * kh;
-  const lds_char* lb = (lds_char*)lo_lds + (lane & 31) * kPitch + 16 * kh;
-  f32x16 acc = f32x16{};
+    // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32): A = W_UV rows (registers), B = merged latent (LDS)
+    const int b = b0 + (lane & 31);
+    const bool bok = (lane & 31) < kRowsPerWg && b < batch;
+    const lds_char* hb = (lds_char*)hi_lds + (lane & 31) * kPitch + 16 * kh;
+    const lds_char* lb = (lds_char*)lo_lds + (lane & 31) * kPitch + 16 * kh;
+    f32x16 acc = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < kDc / 16; ++ks) {
-    const bf16x8 bh = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(hb + 32 * ks);
-    const bf16x8 bl = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lb + 32 * ks);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bl, acc, 0, 0, 0);
-  }
-  // D: lane holds sequence b (column) and output dims 32 wave + 8 q + 4 kh + (0..3)
-  if (bok) {
-    uint16_t* dst = out + ((int64_t)b * n_heads + h) * kDv + 32 * wave;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
-      *reinterpret_cast<uint2*>(dst + 8 * q + 4 * kh) = make_uint2(w0, w1);
+    for (int ks = 0; ks < kDc / 16; ++ks) {
+      const bf16x8 bh = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(hb + 32 * ks);
+      const bf16x8 bl = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lb + 32 * ks);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bl, acc, 0, 0, 0);
     }
+    // D: lane holds sequence b (column) and output dims 32 wave + 8 q + 4 kh + (0..3)
+    if (bok) {
+      uint16_t* dst = out + ((int64_t)b * n_heads + h) * kDv + 32 * wave;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
+        *reinterpret_cast<uint2*>(dst + 8 * q + 4 * kh) = make_uint2(w0, w1);
+      }
+    }
+    __syncthreads();  // the next block rewrites the merged rows
   }
 }
 
@@ -151,10 +159,14 @@ hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t
                           const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
                           hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  const int yb = (batch + kRowsPerWg - 1) / kRowsPerWg;
+  // 16-sequence blocks per work-group: one for small batches; with many rows (prefill) enough that
+  // about 512 work-groups each load their W_UV rows once
+  const int64_t nblk = (batch + kRowsPerWg - 1) / kRowsPerWg;
+  const int64_t bpw = std::max<int64_t>(1, (nblk * n_heads + 511) / 512);
+  const int64_t yb = (nblk + bpw - 1) / bpw;
   if (yb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_mfma_kernel, dim3(n_heads, yb), dim3(256), 0, stream, batch, n_heads, num_splits,
-                     o_partial, lse_partial, w_uv, out, lse_out);
+  hipLaunchKernelGGL(combine_mfma_kernel, dim3(n_heads, (unsigned)yb), dim3(256), 0, stream, batch, n_heads, num_splits,
+                     (int)bpw, o_partial, lse_partial, w_uv, out, lse_out);
   return hipGetLastError();
 }
 

@@ -323,3 +323,43 @@ def test_absorb_then_attend_equals_decode_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(o_part, ref_o)
     assert torch.equal(lse_part, ref_l)
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """The decode step (append, absorb, attend, combine) captured in a HIP graph: every replay, with
+    eager work and synchronisations between replays, reproduces the eager step bit for bit."""
+    say("[decode] step in a HIP graph")
+    case = make_case("graph", 85, 128, [1500, 64, 700], paged=True, spare_blocks=2)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.prepare_step_inputs()
+    st, ns = 256, 6
+    dc.alloc_decode(ns)
+    o_part, lse_part = dc.partials
+
+    def step():
+        dc.append_new()
+        lib.absorb(dc.dims, dc.q_nope, dc.q_rope, dc.w_uk, dc._ws)
+        lib.decode_attend(dc.dims, dc.cache, dc.seq_lens, dc._ws, st, ns, o_part, lse_part)
+        lib.decode_combine(dc.dims, case.batch, ns, o_part, lse_part, dc.w_uv, dc.out, dc.lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = dc.out.clone(), dc.lse.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        dc.out.fill_(0)
+        dc.lse.fill_(0)
+        o_part.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dc.out, ref_out), f"replay {rep}: out differs"
+        assert torch.equal(dc.lse, ref_lse), f"replay {rep}: lse differs"
