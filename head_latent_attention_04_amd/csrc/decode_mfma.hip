@@ -184,49 +184,46 @@ __device__ __forceinline__ float q_elem(const uint16_t* __restrict__ q, int tile
   return bf16_to_f32(q[((int64_t)row * n_heads + h) * kRow + d]);
 }
 
-// Exact two-pass fallback for one wave's 32 heads over tokens [t0, t1): pass 1 finds the true max,
-// pass 2 accumulates exp2(s - max) c_t in fp32. Each lane holds latent columns lane + 64k. Reads the
-// cache rows from global memory; only used when the fast path's fixed reference max is exceeded.
+// Exact two-pass fallback for one head over tokens [t0, t1): pass 1 finds the true max, pass 2
+// accumulates exp2(s - max) c_t in fp32. Each lane holds latent columns lane + 64k. Reads the cache
+// rows from global memory; only used for a head whose scores outgrew the fast path's fixed
+// reference max.
 template <bool kOperandOrder>
-__device__ __forceinline__ void exact_split_fallback(const CacheView& cache, int b, int qrow, int t0, int t1,
-                                                  int n_heads, int h0, const uint16_t* __restrict__ q_abs,
-                                                  float scale_log2, int num_splits, int s,
-                                                  uint16_t* __restrict__ o_partial, float* __restrict__ lse_partial,
-                                                  int lane) {
+__device__ __forceinline__ void exact_head_fallback(const CacheView& cache, int b, int qrow, int t0, int t1,
+                                                    int n_heads, int h, const uint16_t* __restrict__ q_abs,
+                                                    float scale_log2, int num_splits, int s,
+                                                    uint16_t* __restrict__ o_partial, float* __restrict__ lse_partial,
+                                                    int lane) {
   const int tiles = q_tiles(n_heads);
-  for (int hh = 0; hh < 32; ++hh) {
-    const int h = h0 + hh;
-    if (h >= n_heads) break;
-    float qv[9];
+  float qv[9];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) qv[k] = q_elem<kOperandOrder>(q_abs, tiles, n_heads, qrow, h, lane + 64 * k);
-    float m = -INFINITY;
-    for (int t = t0; t < t1; ++t) {
-      const uint16_t* row = cache.data + row_offset(cache, b, t);
-      float part = 0.f;
+  for (int k = 0; k < 9; ++k) qv[k] = q_elem<kOperandOrder>(q_abs, tiles, n_heads, qrow, h, lane + 64 * k);
+  float m = -INFINITY;
+  for (int t = t0; t < t1; ++t) {
+    const uint16_t* row = cache.data + row_offset(cache, b, t);
+    float part = 0.f;
 #pragma unroll
-      for (int k = 0; k < 9; ++k) part = fmaf(qv[k], bf16_to_f32(row[lane + 64 * k]), part);
-      for (int x = 32; x > 0; x >>= 1) part += __shfl_xor(part, x);
-      m = fmaxf(m, part * scale_log2);
-    }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int t = t0; t < t1; ++t) {
-      const uint16_t* row = cache.data + row_offset(cache, b, t);
-      float part = 0.f;
-#pragma unroll
-      for (int k = 0; k < 9; ++k) part = fmaf(qv[k], bf16_to_f32(row[lane + 64 * k]), part);
-      for (int x = 32; x > 0; x >>= 1) part += __shfl_xor(part, x);
-      const float p = exp2f(part * scale_log2 - m);
-      l += p;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = fmaf(p, bf16_to_f32(row[lane + 64 * k]), acc[k]);
-    }
-    const int64_t prow = ((int64_t)qrow * n_heads + h) * num_splits + s;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o_partial[prow * kDc + lane + 64 * k] = f32_to_bf16(acc[k] / l);
-    if (lane == 0) lse_partial[prow] = (m + __log2f(l)) * kLn2;
+    for (int k = 0; k < 9; ++k) part = fmaf(qv[k], bf16_to_f32(row[lane + 64 * k]), part);
+    for (int x = 32; x > 0; x >>= 1) part += __shfl_xor(part, x);
+    m = fmaxf(m, part * scale_log2);
   }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    const uint16_t* row = cache.data + row_offset(cache, b, t);
+    float part = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) part = fmaf(qv[k], bf16_to_f32(row[lane + 64 * k]), part);
+    for (int x = 32; x > 0; x >>= 1) part += __shfl_xor(part, x);
+    const float p = exp2f(part * scale_log2 - m);
+    l += p;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(p, bf16_to_f32(row[lane + 64 * k]), acc[k]);
+  }
+  const int64_t prow = ((int64_t)qrow * n_heads + h) * num_splits + s;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o_partial[prow * kDc + lane + 64 * k] = f32_to_bf16(acc[k] / l);
+  if (lane == 0) lse_partial[prow] = (m + __log2f(l)) * kLn2;
 }
 
 }  // namespace
@@ -238,10 +235,9 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
                    const int32_t* __restrict__ cu_q_lens, int batch, const uint16_t* __restrict__ q_abs,
                    float scale_log2, int split_tokens, int num_splits, uint16_t* __restrict__ o_partial,
                    float* __restrict__ lse_partial) {
+  constexpr int kPBytes = HT * 32 * kPHeadBytes;  // weights P of one stage
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) char p_raw[HT * 32 * kPHeadBytes];
-  __shared__ float inv_lds[HT * 32];
-  __shared__ int restart_flag;
+  __shared__ __attribute__((aligned(16))) char p_raw[2 * kPBytes];  // P of two stages
   lds_char* lds = (lds_char*)smem_raw;
   lds_char* pl = (lds_char*)p_raw;
 
@@ -314,7 +310,6 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
   const int nstages = (t1 - t0 + kStageTok - 1) / kStageTok;
   const int blk0 = t0 / kBlock;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  if (threadIdx.x == 0) restart_flag = 0;
   // Stage 0 goes out right behind the query loads. The empty asm below reads the last query
   // register, so the compiler waits for every load here (the query, and stage 0 with it, which the
   // first step needs anyway) and knows the query is resident inside the loop; otherwise it would
@@ -356,13 +351,12 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
 
   // Online softmax against a reference max m_ref (log2 units) fixed by the first scored stage.
   // Weights are exp2(s - m_ref) <= 2^kMaxExcess, so the accumulators are never rescaled in the loop.
-  // If a later stage's max exceeds m_ref + kMaxExcess, every wave of the work-group discards its
-  // accumulators and the scoring waves recompute their heads with the exact fallback (in practice
-  // never taken).
+  // A head whose later scores exceed m_ref + kMaxExcess is flagged; its column of the accumulators
+  // is left alone (the MFMA keeps columns apart) and the head is recomputed by the exact fallback
+  // after the split's other heads are written (in practice never taken).
   float m_ref = -INFINITY;
   float lsum = 0.f;
   bool overflow = false;
-  bool restart = false;
   f32x16 o[4 * HT];  // O^T tiles: latent columns 128 wave + 32 dt, head tile ht -> o[dt * HT + ht]
 #pragma unroll
   for (int i = 0; i < 4 * HT; ++i) o[i] = f32x16{};
@@ -379,36 +373,36 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     tlo = lds_tr16(stp + pv_base[g & 1][0] + off);
     thi = lds_tr16(stp + pv_base[g & 1][1] + off);
   };
-  auto pv_begin = [&](const lds_char* stp) {
+  auto pv_begin = [&](const lds_char* stp, const lds_char* pp) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) pb[ht] = lds_b128(pl + pb_base[0] + ht * 32 * kPHeadBytes);
+    for (int ht = 0; ht < HT; ++ht) pb[ht] = lds_b128(pp + pb_base[0] + ht * 32 * kPHeadBytes);
     tr_load(stp, 0);
   };
-  auto pv_mfma = [&](const lds_char* stp, int i) {
+  auto pv_mfma = [&](const lds_char* stp, const lds_char* pp, int i) {
     const int ksp = i / (4 * HT), dt = (i / HT) % 4, ht = i % HT;
     if (ht == 0) {
       ta = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7));
       if (i / HT + 1 < 8) tr_load(stp, i / HT + 1);
     }
     o[dt * HT + ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, pb[ht], o[dt * HT + ht], 0, 0, 0);
-    if (ksp == 0 && dt == 3) pb[ht] = lds_b128(pl + pb_base[1] + ht * 32 * kPHeadBytes);
+    if (ksp == 0 && dt == 3) pb[ht] = lds_b128(pp + pb_base[1] + ht * 32 * kPHeadBytes);
   };
-  auto pv_all = [&](const lds_char* stp) {
-    pv_begin(stp);
+  auto pv_all = [&](const lds_char* stp, const lds_char* pp) {
+    pv_begin(stp, pp);
 #pragma unroll
-    for (int i = 0; i < 8 * HT; ++i) pv_mfma(stp, i);
+    for (int i = 0; i < 8 * HT; ++i) pv_mfma(stp, pp, i);
   };
 
   // The loop is software-pipelined by one stage: step k scores stage k and, interleaved with those
   // MFMAs and with the softmax that follows them, reduces stage k-1 with the weights P(k-1) written
-  // at the end of step k-1. Step 0 reduces a zero stage with zero weights (buffer 3 and P are
-  // cleared here), which adds nothing. Step k also copies stage k+2 into the buffer of stage k-2,
+  // at the end of step k-1 (P has two buffers, so one barrier per step suffices). Step 0 reduces a
+  // zero stage with zero weights (buffer 3 and P buffer 1 are cleared here), which adds nothing. Step k also copies stage k+2 into the buffer of stage k-2,
   // one instruction every fourth score MFMA, so no wave stalls on a burst of copy instructions.
   {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < HT * 32 * kPHeadBytes / 16; i += kWaves * 64)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(pl + 16 * i) = z;
+    for (int i = threadIdx.x; i < kPBytes / 16; i += kWaves * 64)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(pl + kPBytes + 16 * i) = z;
     for (int i = threadIdx.x; i < kStageBytes / 16; i += kWaves * 64)
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (kStages - 1) * kStageBytes + 16 * i) = z;
   }
@@ -421,9 +415,9 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     else
       wait_vmcnt<0>();
     wg_barrier();  // publishes stage k and P(k-1); every wave is done with stage k-2 and P(k-2)
-    restart |= restart_flag != 0;
     const lds_char* st = lds + (k % kStages) * kStageBytes;
     const lds_char* stp = lds + ((k + kStages - 1) % kStages) * kStageBytes;  // stage k-1
+    const lds_char* pp = pl + ((k + 1) & 1) * kPBytes;                        // P(k-1)
     const bool copy_next = k + 2 < nstages;
     StageCopy cp;
     if (copy_next) {
@@ -434,7 +428,7 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
 
     // every wave runs this body; a wave without a head tile scores a duplicate and drops it
     const int valid = min(kStageTok, t1 - t0 - k * kStageTok);
-    pv_begin(stp);
+    pv_begin(stp, pp);
     // ---- scores S^T[32 tokens x 32 heads]; half of stage k-1's reduction and the copy interleaved
     f32x16 sacc;
     {
@@ -452,7 +446,7 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
         else
           score_mfma(sacc, a, qreg[ks]);
 #pragma unroll
-        for (int i = ks * kHalfPv / 36; i < (ks + 1) * kHalfPv / 36; ++i) pv_mfma(stp, i);
+        for (int i = ks * kHalfPv / 36; i < (ks + 1) * kHalfPv / 36; ++i) pv_mfma(stp, pp, i);
         if ((ks & 3) == 1 && copy_next) stage_copy_band(cp, ks >> 2);
         // keep this order: the scheduler would otherwise hoist operand loads and run out of registers
         __builtin_amdgcn_sched_barrier(0);
@@ -463,7 +457,7 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     // of stage k-1's reduction runs on the matrix cores meanwhile (12 slots).
     auto pv_slot = [&](int slot) {
 #pragma unroll
-      for (int i = kHalfPv + slot * kHalfPv / 12; i < kHalfPv + (slot + 1) * kHalfPv / 12; ++i) pv_mfma(stp, i);
+      for (int i = kHalfPv + slot * kHalfPv / 12; i < kHalfPv + (slot + 1) * kHalfPv / 12; ++i) pv_mfma(stp, pp, i);
       __builtin_amdgcn_sched_barrier(0);
     };
     if (valid < kStageTok) {  // only the split's last, partly filled stage needs a mask
@@ -493,33 +487,31 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
       pv_slot(3 + (j >> 1));
     }
     pv_slot(11);
-    if (qk_wave && __any(overflow) && lane == 0) restart_flag = 1;
-    wg_barrier();  // every wave is done with stage k-1 and P(k-1)
-    if (qk_wave) {  // P(k)[head][tokens 8 q + 4 kh .. +3] <- (pw[2q], pw[2q+1])
+    if (qk_wave) {  // P(k)[head][tokens 8 q + 4 kh .. +3] <- (pw[2q], pw[2q+1]), into the other buffer
       const int ps = p_swz(n);
+      lds_char* pk = pl + (k & 1) * kPBytes;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(pl + hl * kPHeadBytes + 16 * (q ^ ps) + 8 * kh) =
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(pk + hl * kPHeadBytes + 16 * (q ^ ps) + 8 * kh) =
             u32x2{pw[2 * q], pw[2 * q + 1]};
     }
   }
   wg_barrier();  // publishes P of the last stage
-  pv_all(lds + ((nstages - 1) % kStages) * kStageBytes);
+  pv_all(lds + ((nstages - 1) % kStages) * kStageBytes, pl + ((nstages - 1) & 1) * kPBytes);
   wg_barrier();  // every wave is done with the stages and P
-  restart |= restart_flag != 0;
+  // explicit wait states before the VALU reads the output accumulators (the count the compiler
+  // derives from the instructions in between is not relied on)
+#pragma unroll
+  for (int i = 0; i < 4 * HT; ++i) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[i]));
 
-  if (restart) {
-    if (qk_wave)
-      exact_split_fallback<kOperandOrder>(cache, b, qrow, t0, t1, n_heads, h0 + 32 * wave, q_abs, scale_log2,
-                                          num_splits, s, o_partial, lse_partial, lane);
-    return;
-  }
-
+  // 1/lsum of every head (negative: the head overflowed and is recomputed below), in P's space
+  float* inv_lds = reinterpret_cast<float*>(p_raw);
   if (qk_wave) {
     lsum += __shfl_xor(lsum, 32);
     if (kh == 0) {
-      inv_lds[hl] = 1.f / lsum;
-      if (hok) lse_partial[((int64_t)qrow * n_heads + head) * num_splits + s] = (m_ref + __log2f(lsum)) * kLn2;
+      inv_lds[hl] = overflow ? -1.f : 1.f / lsum;
+      if (hok && !overflow)
+        lse_partial[((int64_t)qrow * n_heads + head) * num_splits + s] = (m_ref + __log2f(lsum)) * kLn2;
     }
   }
   wg_barrier();  // publishes 1/lsum of every head
@@ -547,9 +539,19 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
 #pragma unroll 4
   for (int i = 0; i < 8 * HT; ++i) {
     const int r = 4 * i + wave;
-    if (r < 32 * tiles_here && h0 + r < n_heads) {
+    if (r < 32 * tiles_here && h0 + r < n_heads && inv_lds[r] >= 0.f) {
       const uint4 v = *reinterpret_cast<const uint4*>(smem_raw + r * kOutPitch + 16 * lane);
       reinterpret_cast<uint4*>(o_partial + (((int64_t)qrow * n_heads + h0 + r) * num_splits + s) * kDc)[lane] = v;
+    }
+  }
+  // heads whose scores outgrew the reference max: exact recomputation by the wave that scored them
+  if (qk_wave) {
+    uint64_t todo = __ballot(overflow && kh == 0 && hok);
+    while (todo) {
+      const int hh = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      exact_head_fallback<kOperandOrder>(cache, b, qrow, t0, t1, n_heads, h0 + 32 * wave + hh, q_abs, scale_log2,
+                                         num_splits, s, o_partial, lse_partial, lane);
     }
   }
 }
