@@ -3,6 +3,9 @@
   python3 -m head_latent_attention_04_amd.profiling stats <run_kernel_stats.csv> --title T --command C
       prints the per-kernel duration table (microseconds) with the command that produced it.
 
+  python3 -m head_latent_attention_04_amd.profiling counters <run_counter_collection.csv>... --kernel NAME --command C
+      prints the average per-dispatch value of every collected counter for kernels named NAME.
+
   python3 -m head_latent_attention_04_amd.profiling traffic --fetch <fetch run_counter_collection.csv>
       --write <write run_counter_collection.csv> --kernel NAME --workload W --copy-bytes N --command C
       prints the JSON that bench.py reads as the attention kernel's measured HBM traffic: the average
@@ -79,6 +82,20 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, copy_byt
     return res
 
 
+def counters(paths, kernel: str, command: str) -> str:
+    """Average per-dispatch value of every counter in the given counter-collection CSVs for kernels
+    whose name contains `kernel`."""
+    out = [f"# counters of {kernel} (average per dispatch)", f"# command: {command}"]
+    for path in paths:
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for c, xs in sorted(vals.items()):
+            out.append(f"{c:28s} {sum(xs) / len(xs):16.1f}   ({len(xs)} dispatches)")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="rocprofv3 summaries for profiles/")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -93,8 +110,14 @@ def main(argv=None):
     b.add_argument("--workload", required=True)
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args(argv)
-    if args.cmd == "stats":
+    if args.cmd == "counters":
+        print(counters(args.csv, args.kernel, args.command))
+    elif args.cmd == "stats":
         print(stats(args.csv, args.title, args.command))
     else:
         print(json.dumps(traffic(args.fetch, args.write, args.kernel, args.workload, args.copy_bytes, args.command),
