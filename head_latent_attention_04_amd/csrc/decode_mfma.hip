@@ -39,6 +39,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kWaves = 4;                           // waves per work-group
@@ -399,7 +400,6 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
   // zero stage with zero weights (buffer 3 and P buffer 1 are cleared here), which adds nothing. Step k also copies stage k+2 into the buffer of stage k-2,
   // one instruction every fourth score MFMA, so no wave stalls on a burst of copy instructions.
   {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = threadIdx.x; i < kPBytes / 16; i += kWaves * 64)
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(pl + kPBytes + 16 * i) = z;
@@ -535,13 +535,16 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     }
   }
   wg_barrier();
-  // whole 1 KB rows out: wave w writes the group's heads w, w + 4, ...
+  // whole 1 KB rows out: wave w writes the group's heads w, w + 4, ... The stores are nontemporal:
+  // the partials are read once, by the combine kernel on other XCDs, so they are not kept in this
+  // XCD's L2 (which would otherwise write them back when the kernel ends).
 #pragma unroll 4
   for (int i = 0; i < 8 * HT; ++i) {
     const int r = 4 * i + wave;
     if (r < 32 * tiles_here && h0 + r < n_heads && inv_lds[r] >= 0.f) {
-      const uint4 v = *reinterpret_cast<const uint4*>(smem_raw + r * kOutPitch + 16 * lane);
-      reinterpret_cast<uint4*>(o_partial + (((int64_t)qrow * n_heads + h0 + r) * num_splits + s) * kDc)[lane] = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem_raw + r * kOutPitch + 16 * lane);
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(o_partial + (((int64_t)qrow * n_heads + h0 + r) * num_splits + s) * kDc) + lane);
     }
   }
   // heads whose scores outgrew the reference max: exact recomputation by the wave that scored them
