@@ -4,14 +4,15 @@
 Workload: decode B=32, n_h=128, d_c=512, d_R=64, d_nope=128, d_v=128, context 4096 per sequence,
 contiguous bf16 latent cache (576 elements per token), synthetic seeded inputs with the shapes of
 the DeepSeek-V2 dimensions. One step = the whole decode hot path on one batch:
-  mla_rope_append (the 32 new tokens: rotate k_R and q_R, write the rows)
-  -> mla_absorb (q absorption through W_UK)
+  mla_rope_append_absorb (the 32 new tokens: rotate k_R and q_R, write the rows; and in the same
+    launch the q absorption through W_UK, i.e. mla_rope_append + mla_absorb)
   -> mla_decode_attend (split-KV attention over the latent cache)
   -> mla_decode_combine (log-sum-exp merge of the splits + W_UV up-projection).
-(mla_absorb + mla_decode_attend is exactly mla_decode.)
+(mla_absorb + mla_decode_attend is exactly mla_decode.) The standalone mla_rope_append and
+mla_absorb kernels are timed per launch beside the step.
 Inputs are resident in HBM before timing starts. Several independent copies of the inputs are
 rotated so that the 256 MB Infinity Cache cannot hold one step's working set. The step is timed
-as eager launches; the same four launches captured in a HIP graph and replayed are reported beside.
+as eager launches; the same three launches captured in a HIP graph and replayed are reported beside.
 
 Prints ONE JSON line. `value` is the step's algorithmic TFLOP/s; latent-KV GB/s, the dominant
 kernel's roofline fraction and the fp64 CPU oracle's rate (on the host's cores) ride along.
@@ -182,9 +183,11 @@ def main():
     def rope(i):
         sets[i % nsets].append_new(reset_q=False)  # the rotation repeats on the rotated query: same work
 
+    def front(i):  # RoPE + append and absorption in one launch (mla_rope_append_absorb)
+        sets[i % nsets].append_absorb_new(reset_q=False)
+
     def step(i):
-        rope(i)
-        absorb(i)
+        front(i)
         attend(i)
         comb(i)
 
@@ -211,9 +214,11 @@ def main():
     ms_step_graph = time_loop(torch, lambda i: graphs[i % nsets].replay(), args.steps)
     ms_step = ms_step_eager
 
-    # each kernel of the step alone, per launch (the absorbed queries of every set are in place)
+    # each kernel of the step alone, per launch (the absorbed queries of every set are in place), and
+    # the standalone RoPE + append and absorption kernels the fused front half replaces
     ms = {}
-    for name, fn in (("rope_append", rope), ("absorb", absorb), ("decode_attention", attend), ("combine_wuv", comb)):
+    for name, fn in (("rope_append_absorb", front), ("decode_attention", attend), ("combine_wuv", comb),
+                     ("rope_append_alone", rope), ("absorb_alone", absorb)):
         for i in range(args.warmup):
             fn(i)
         ms[name] = time_each(torch, fn, args.steps)

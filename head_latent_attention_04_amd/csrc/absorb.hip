@@ -14,9 +14,12 @@
 // slice of W_UK[h] is staged in LDS once (rows padded to 544 bytes so the transposed reads of 4 rows hit
 // different banks) and read with ds_read_b64_tr_b16 as the d-contiguous A operand; q_nope rows are
 // the B operand straight from global memory. fp32 accumulation, one bf16 rounding.
+//
+// rope_absorb_kernel runs the RoPE rotation and cache append of the same tokens (rope_device.h) in
+// the same launch, on work-groups of their own.
 #include <algorithm>
 
-#include "mla_internal.h"
+#include "rope_device.h"
 
 namespace mla {
 
@@ -35,15 +38,14 @@ __device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
 }
 }  // namespace
 
-__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, int rows_per_wg,
-                                                          const uint16_t* __restrict__ q_nope,
-                                                          const uint16_t* __restrict__ q_rope,
-                                                          const uint16_t* __restrict__ w_uk,
-                                                          uint16_t* __restrict__ q_abs) {
-  __shared__ __attribute__((aligned(16))) char w_lds[kDnope * kPitch];
-  const int h = blockIdx.x;
-  const int ch = blockIdx.y;                 // column half
-  const int rbase = blockIdx.z * rows_per_wg;  // this work-group's rows (a multiple of 32)
+constexpr int kAbsorbLds = kDnope * kPitch;  // bytes of LDS one absorption work-group uses
+
+// Work-group (head h, column half ch, rows rbase .. rbase + rows_per_wg - 1). q_rope == nullptr: the
+// RoPE part of the rows is written by someone else (the fused RoPE work-groups).
+__device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, int n_heads, int rows_per_wg,
+                                            const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+                                            const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs,
+                                            char* w_lds) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
   const int tiles = q_tiles(n_heads);
   lds_char* lds = (lds_char*)w_lds;
@@ -86,7 +88,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
     }
   }
   // the RoPE part of the row is copied unchanged (column half 0 does it)
-  if (ch == 0) {
+  if (ch == 0 && q_rope != nullptr) {
     for (int i = tid; i < rows_per_wg * (kDr / 8); i += 256) {
       const int r = rbase + i / (kDr / 8), c8 = i % (kDr / 8);
       if (r < rows)
@@ -142,19 +144,78 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads,
   }
 }
 
-hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
-                         const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream) {
-  if (rows == 0) return hipSuccess;
-  // blocks of 32 rows per work-group: one for small batches, more when there are many rows, so
-  // that about 1024 work-groups each stage their W_UK slice once
+__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, int rows_per_wg,
+                                                          const uint16_t* __restrict__ q_nope,
+                                                          const uint16_t* __restrict__ q_rope,
+                                                          const uint16_t* __restrict__ w_uk,
+                                                          uint16_t* __restrict__ q_abs) {
+  __shared__ __attribute__((aligned(16))) char w_lds[kAbsorbLds];
+  absorb_tile(blockIdx.x, blockIdx.y, blockIdx.z * rows_per_wg, rows, n_heads, rows_per_wg, q_nope, q_rope, w_uk, q_abs,
+              w_lds);
+}
+
+// RoPE + append and absorption in one launch: the first n_rope work-groups are (token, head group)
+// RoPE work-groups that also write the rotated query into the RoPE part of the absorbed rows (row i
+// is token i); the rest are the absorption's (head, column half, row range) work-groups, which leave
+// that part alone. The two sets touch disjoint outputs and run side by side.
+__global__ void __launch_bounds__(256) rope_absorb_kernel(CacheView cache, int n_heads, const int32_t* __restrict__ token_seq,
+                                                          const int32_t* __restrict__ token_pos,
+                                                          const uint16_t* __restrict__ c_kv,
+                                                          const uint16_t* __restrict__ k_rope,
+                                                          uint16_t* __restrict__ q_rope, double log2_theta, int n_rope,
+                                                          int rows, int rows_per_wg, const uint16_t* __restrict__ q_nope,
+                                                          const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs) {
+  __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];
+  const int tiles = q_tiles(n_heads);
+  if ((int)blockIdx.x < n_rope) {
+    const int groups = rope_groups(n_heads);
+    rope_token_group(cache, n_heads, blockIdx.x / groups, blockIdx.x % groups, token_seq, token_pos, c_kv, k_rope,
+                     q_rope, log2_theta, q_abs, tiles, reinterpret_cast<double*>(smem));
+    return;
+  }
+  const int hp = 32 * tiles;
+  const int a = blockIdx.x - n_rope;
+  absorb_tile(a % hp, (a / hp) % (kDc / kCols), (a / (hp * (kDc / kCols))) * rows_per_wg, rows, n_heads, rows_per_wg,
+              q_nope, nullptr, w_uk, q_abs, smem);
+}
+
+namespace {
+// blocks of 32 rows per work-group: one for small batches, more when there are many rows, so that
+// about 1024 work-groups each stage their W_UK slice once
+int absorb_rows_per_wg(int rows, int n_heads) {
   const int hp = 32 * q_tiles(n_heads);
   const int64_t nrb = (rows + 31) / 32;
   const int64_t bpw = std::max<int64_t>(1, (nrb * hp * 2 + 1023) / 1024);
-  const int rows_per_wg = (int)std::min<int64_t>(32 * bpw, 32 * nrb);
+  return (int)std::min<int64_t>(32 * bpw, 32 * nrb);
+}
+}  // namespace
+
+hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
+                         const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int hp = 32 * q_tiles(n_heads);
+  const int rows_per_wg = absorb_rows_per_wg(rows, n_heads);
   const int zb = (rows + rows_per_wg - 1) / rows_per_wg;
   if (zb > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(absorb_mfma_kernel, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, rows_per_wg,
                      q_nope, q_rope, w_uk, q_abs);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_absorb(const CacheView& cache, int n_heads, int num_tokens, const int32_t* token_seq,
+                              const int32_t* token_pos, const uint16_t* c_kv, const uint16_t* k_rope, uint16_t* q_rope,
+                              float theta, const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_abs,
+                              hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int hp = 32 * q_tiles(n_heads);
+  const int rows_per_wg = absorb_rows_per_wg(num_tokens, n_heads);
+  const int64_t zb = (num_tokens + rows_per_wg - 1) / rows_per_wg;
+  const int64_t n_rope = (int64_t)num_tokens * rope_groups(n_heads);
+  const int64_t total = n_rope + (int64_t)hp * (kDc / kCols) * zb;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_absorb_kernel, dim3((unsigned)total), dim3(256), 0, stream, cache, n_heads, token_seq, token_pos,
+                     c_kv, k_rope, q_rope, log2((double)theta), (int)n_rope, num_tokens, rows_per_wg, q_nope, w_uk,
+                     q_abs);
   return hipGetLastError();
 }
 

@@ -7,7 +7,9 @@
 // section 四: the W_UV up-projection or its absorbed equivalent).
 //
 // One work-group per (head, range of 16-sequence blocks), 4 waves:
-//   0. each wave loads its 32 rows of W_UV[h] into registers first (latency overlaps step 1);
+//   0. every load a block needs is issued before any is used: the wave's 32 rows of W_UV[h] (once;
+//      kept in registers across blocks), the log-sum-exps and the partials of the first 8 splits,
+//      so one memory round trip covers them all;
 //   1. merge: thread t merges latent columns [32 (t % 16), +32) of sequence t / 16 (fp32) and
 //      stores them in LDS as a bf16 pair hi + lo (hi = bf16(o), lo = bf16(o - hi)), which carries
 //      the merged latent to the MFMA with about 16 significant bits;
@@ -27,9 +29,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kRowsPerWg = 16;  // sequences per work-group (MFMA columns 16..31 unused)
 constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded (conflict-free b128 reads)
+constexpr int kChunk = 8;             // splits whose partials are loaded together
 }  // namespace
 
-__global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_heads, int num_splits, int blocks_per_wg,
+__global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_heads, int num_splits, int blocks_per_wg,
                                                            const uint16_t* __restrict__ o_partial,
                                                            const float* __restrict__ lse_partial,
                                                            const uint16_t* __restrict__ w_uv,
@@ -39,8 +42,7 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
   const int h = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
 
-  // W_UV rows of the up-projection (A operand: row v = 32 wave + lane % 32, columns 16 ks + 8 kh ..
-  // +7), loaded first so their latency overlaps the merge.
+  // W_UV rows of the up-projection (A operand: row v = 32 wave + lane % 32, columns 16 ks + 8 kh .. +7)
   bf16x8 wa[kDc / 16];
   {
     const uint4* wrow = reinterpret_cast<const uint4*>(w_uv + ((int64_t)h * kDv + 32 * wave + (lane & 31)) * kDc + 8 * kh);
@@ -69,44 +71,66 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int batch, int n_head
       const bool bok = b < batch;
       const int c0 = 32 * (tid & 15);
       const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
+      // the first kChunk splits: log-sum-exps and partials issued together, without branches (an
+      // index past the last split reads the last one and gets weight zero), so one wait covers them
+      float ls[kChunk];
+      uint4 v[kChunk][4];
+#pragma unroll
+      for (int q = 0; q < kChunk; ++q) {
+        const float l = lse_partial[base + min(q, num_splits - 1)];
+        ls[q] = q < num_splits ? l : -INFINITY;
+      }
+#pragma unroll
+      for (int q = 0; q < kChunk; ++q) {
+        const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(q, num_splits - 1)) * kDc + c0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[q][k] = src[k];
+      }
       float m = -INFINITY;
-      for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
+#pragma unroll
+      for (int q = 0; q < kChunk; ++q) m = fmaxf(m, ls[q]);
+      for (int s = kChunk; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
       float z = 0.f;
-      if (m != -INFINITY)
-        for (int s = 0; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) z += ls[q] == -INFINITY ? 0.f : __expf(ls[q] - m);
+        for (int s = kChunk; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
+      }
       if ((tid & 15) == 0 && bok && lse_out)
         lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
       const float inv_z = (m == -INFINITY) ? 0.f : 1.f / z;
       float acc[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-      if (bok && m != -INFINITY) {
-        // splits four at a time, every load of a group issued before the first multiply-add
-        for (int s0 = 0; s0 < num_splits; s0 += 4) {
-          uint4 v[4][4];
-          float wgt[4];
+      auto accumulate = [&](float wgt, const uint4 (&vq)[4]) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int s = s0 + q;
-            const float ls = s < num_splits ? lse_partial[base + s] : -INFINITY;
-            wgt[q] = ls == -INFINITY ? 0.f : __expf(ls - m) * inv_z;
-            const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(s, num_splits - 1)) * kDc + c0);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t wv[4] = {vq[k].x, vq[k].y, vq[k].z, vq[k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[8 * k + 2 * e] = fmaf(wgt, __uint_as_float(wv[e] << 16), acc[8 * k + 2 * e]);
+            acc[8 * k + 2 * e + 1] = fmaf(wgt, __uint_as_float(wv[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+          }
+        }
+      };
+      if (bok && m != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q)  // an empty split (lse = -inf) contributes nothing
+          if (ls[q] != -INFINITY) accumulate(__expf(ls[q] - m) * inv_z, v[q]);
+        // further splits, kChunk at a time, every load of a chunk issued before the first multiply-add
+        for (int s0 = kChunk; s0 < num_splits; s0 += kChunk) {
+#pragma unroll
+          for (int q = 0; q < kChunk; ++q) {
+            const int s = min(s0 + q, num_splits - 1);
+            const float l = lse_partial[base + s];
+            ls[q] = s0 + q < num_splits ? l : -INFINITY;
+            const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + s) * kDc + c0);
 #pragma unroll
             for (int k = 0; k < 4; ++k) v[q][k] = src[k];
           }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (wgt[q] == 0.f) continue;  // empty split (or past the end): contributes nothing
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t wv[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                acc[8 * k + 2 * e] = fmaf(wgt[q], __uint_as_float(wv[e] << 16), acc[8 * k + 2 * e]);
-                acc[8 * k + 2 * e + 1] = fmaf(wgt[q], __uint_as_float(wv[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
-              }
-            }
-          }
+          for (int q = 0; q < kChunk; ++q)
+            if (ls[q] != -INFINITY) accumulate(__expf(ls[q] - m) * inv_z, v[q]);
         }
       }
       char* hrow = hi_lds + bl * kPitch + c0 * 2;

@@ -123,6 +123,24 @@ int mla_absorb(const mla_dims* dims, int32_t rows, const uint16_t* q_nope, const
                                      stream));
 }
 
+int mla_rope_append_absorb(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens, const int32_t* token_seq,
+                           const int32_t* token_pos, const uint16_t* c_kv, const uint16_t* k_rope,
+                           uint16_t* q_rope_inout, const uint16_t* q_nope, const uint16_t* w_uk, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535 * 128) return MLA_ERR_BAD_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!token_seq || !token_pos || !c_kv || !k_rope || !q_rope_inout || !q_nope || !w_uk || !workspace)
+    return MLA_ERR_NULL;
+  if (workspace_bytes < mla_decode_workspace_size(dims, num_tokens)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_rope_absorb(view(cache), dims->n_heads, num_tokens, token_seq, token_pos, c_kv, k_rope,
+                                          q_rope_inout, dims->rope_theta, q_nope, w_uk,
+                                          static_cast<uint16_t*>(workspace), stream));
+}
+
 int mla_decode_attend(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
                       const void* workspace, size_t workspace_bytes, int32_t split_tokens, int32_t num_splits,
                       uint16_t* o_partial, float* lse_partial, hipStream_t stream) {

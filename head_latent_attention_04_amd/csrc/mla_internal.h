@@ -72,6 +72,13 @@ hipError_t launch_rope_append(const CacheView& cache, int n_heads, int num_token
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
                          const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream);
 
+// launch_rope_append (with the query) and launch_absorb of the same num_tokens rows in one launch:
+// row i of q_abs is token i, its RoPE part the query launch_rope_append rotates in place.
+hipError_t launch_rope_absorb(const CacheView& cache, int n_heads, int num_tokens, const int32_t* token_seq,
+                              const int32_t* token_pos, const uint16_t* c_kv, const uint16_t* k_rope, uint16_t* q_rope,
+                              float theta, const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_abs,
+                              hipStream_t stream);
+
 // Split-KV attention over the latent cache with bf16 MFMA. Row r of the work is one query token:
 // decode (cu_q_lens == nullptr): row r is sequence r and sees its seq_lens[r] tokens; prefill: row j
 // is query token j (sequence located through cu_q_lens[0..batch]) and sees tokens 0..its position.

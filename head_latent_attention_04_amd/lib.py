@@ -50,6 +50,8 @@ EXPORTS = {
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp, _i32,
                                   _i32, _vp, _sz, _vp, _vp, _vp]),
     "mla_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_rope_append_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_decode_attend": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _sz, _i32,
                                          _i32, _vp, _vp, _vp]),
     "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
@@ -170,6 +172,19 @@ def absorb(dims: MlaDims, q_nope, q_rope, w_uk, workspace, stream=None):
         _ptr(q_rope, "q_rope", BF16, R * H * dims.d_rope), _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_absorb", st)
+
+
+def rope_append_absorb(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_rope, q_rope, q_nope, w_uk,
+                       workspace, stream=None):
+    T = token_seq.numel()
+    H = dims.n_heads
+    st = load().mla_rope_append_absorb(
+        ctypes.byref(dims), ctypes.byref(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        _ptr(token_pos, "token_pos", I32, T), _ptr(c_kv, "c_kv", BF16, T * dims.d_c),
+        _ptr(k_rope, "k_rope", BF16, T * dims.d_rope), _ptr(q_rope, "q_rope", BF16, T * H * dims.d_rope),
+        _ptr(q_nope, "q_nope", BF16, T * H * dims.d_nope), _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mla_rope_append_absorb", st)
 
 
 def decode_attend(dims: MlaDims, cache: MlaCache, seq_lens, workspace, split_tokens: int, num_splits: int, o_partial,

@@ -82,6 +82,16 @@ class DeviceCase:
         lib.rope_append(self.dims, self.cache, self.step_seq, self.step_pos, self.step_c, self.step_k, self.q_rope,
                         stream)
 
+    def append_absorb_new(self, stream=None, reset_q: bool = True):
+        """append_new and the absorption of the new tokens' queries in one launch
+        (mla_rope_append_absorb); the workspace must be allocated by alloc_decode."""
+        if reset_q:
+            self.q_rope.copy_(self.q_rope_raw)
+        if not hasattr(self, "step_seq"):
+            self.prepare_step_inputs()
+        lib.rope_append_absorb(self.dims, self.cache, self.step_seq, self.step_pos, self.step_c, self.step_k,
+                               self.q_rope, self.q_nope, self.w_uk, self._ws, stream)
+
     # -- decode -------------------------------------------------------------------------------
     def plan(self, num_cus: int = 256) -> Tuple[int, int]:
         return lib.decode_plan(self.dims, self.case.batch, int(self.case.seq_lens.max()), num_cus)

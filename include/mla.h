@@ -153,6 +153,23 @@ int mla_decode_attend(const mla_dims* dims, const mla_cache* cache, int32_t batc
                       uint16_t* o_partial, float* lse_partial, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mla_rope_append_absorb - mla_rope_append of new tokens followed by mla_absorb of the same tokens,
+ * in one launch (the step's front half: "淺析DeepSeek多頭潛在注意力機制（MLA）", "MLA與ROPE的融合"
+ * rotates the decoupled key and query; "论文复现工坊 No.4", section 4 absorbs W_UK into the query).
+ * Row i of the absorption is token i (decode: one new token per sequence, token i of sequence i):
+ *   cache, token_seq, token_pos, c_kv, k_rope  as for mla_rope_append
+ *   q_rope_inout [num_tokens, n_heads, d_rope] bf16, rotated in place (required here)
+ *   q_nope       [num_tokens, n_heads, d_nope] bf16;  w_uk as for mla_decode
+ *   workspace    >= mla_decode_workspace_size(dims, num_tokens) bytes, 256-byte aligned; afterwards it
+ *                holds what mla_absorb(rows = num_tokens) on the rotated queries leaves there, bit for bit
+ * The cache, q_rope_inout and workspace end up exactly as after mla_rope_append then mla_absorb.
+ * ------------------------------------------------------------------------------------------- */
+int mla_rope_append_absorb(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens,
+                           const int32_t* token_seq, const int32_t* token_pos, const uint16_t* c_kv,
+                           const uint16_t* k_rope, uint16_t* q_rope_inout, const uint16_t* q_nope,
+                           const uint16_t* w_uk, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mla_decode_absorbed - mla_decode for callers that already hold the absorbed queries, e.g. with
  * W_UK folded into the query up-projection ahead of time ("淺析DeepSeek多頭潛在注意力機制（MLA）",
  * "MLA的數學原理": x_t (W_q W_k^T) is one precomputable product).

@@ -325,6 +325,35 @@ def test_absorb_then_attend_equals_decode_bitwise():
     assert torch.equal(lse_part, ref_l)
 
 
+@pytest.mark.parametrize("n_heads", [128, 48])
+def test_rope_append_absorb_equals_separate_calls_bitwise(n_heads):
+    """mla_rope_append_absorb leaves the cache, the rotated queries and the absorbed-query workspace
+    exactly as mla_rope_append followed by mla_absorb (48 heads: a padded head tile and a partial
+    RoPE head group)."""
+    say(f"[rope_append_absorb] fused front half, n_heads={n_heads}")
+    case = make_case("fused_front", 86 + n_heads, n_heads, [700, 1, 64, 2100, 4097], paged=True, spare_blocks=3)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.prepare_step_inputs()
+    dc.alloc_decode(4)
+    torch.cuda.synchronize()
+    cache0 = dc.cache_data.clone()
+    nbytes = lib.decode_workspace_size(dc.dims, case.batch)
+    dc.append_new()
+    lib.absorb(dc.dims, dc.q_nope, dc.q_rope, dc.w_uk, dc._ws)
+    torch.cuda.synchronize()
+    ref_cache, ref_q, ref_ws = dc.cache_data.clone(), dc.q_rope.clone(), dc._ws[:nbytes].clone()
+    dc.cache_data.copy_(cache0)
+    dc.q_rope.copy_(dc.q_rope_raw)
+    dc._ws.fill_(0x5A)
+    lib.rope_append_absorb(dc.dims, dc.cache, dc.step_seq, dc.step_pos, dc.step_c, dc.step_k, dc.q_rope, dc.q_nope,
+                           dc.w_uk, dc._ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dc.cache_data, ref_cache)
+    assert torch.equal(dc.q_rope, ref_q)
+    assert torch.equal(dc._ws[:nbytes], ref_ws)
+
+
 def test_decode_step_graph_replay_matches_eager():
     """The decode step (append, absorb, attend, combine) captured in a HIP graph: every replay, with
     eager work and synchronisations between replays, reproduces the eager step bit for bit."""
