@@ -7,15 +7,15 @@
 // section 四: the W_UV up-projection or its absorbed equivalent).
 //
 // One work-group per (head, range of 16-sequence blocks), 4 waves:
-//   0. every load a block needs is issued before any is used: the wave's 32 rows of W_UV[h] (once;
-//      kept in registers across blocks), the log-sum-exps and the partials of the first 8 splits,
-//      so one memory round trip covers them all;
+//   0. every load a block needs is issued before any is used: the log-sum-exps and the partials of
+//      its first 8 splits, then (first block only) the wave's 32 rows of W_UV[h], kept in registers
+//      across blocks; the merge waits only for the partials and overlaps W_UV's arrival;
 //   1. merge: thread t merges latent columns [32 (t % 16), +32) of sequence t / 16 (fp32) and
 //      stores them in LDS as a bf16 pair hi + lo (hi = bf16(o), lo = bf16(o - hi)), which carries
 //      the merged latent to the MFMA with about 16 significant bits;
-//   2. up-projection with bf16 MFMA: out^T[v, b] = W_UV[h][v, :] . o_lat[b, :] for the wave's 32
-//      output columns v (M = v, N = b padded to 32 with zero rows, K = c), hi and lo accumulated
-//      into the same fp32 tile.
+//   2. up-projection with bf16 MFMA (v_mfma_f32_16x16x32_bf16): out^T[v, b] = W_UV[h][v, :] . o_lat[b, :]
+//      for the wave's 32 output columns v (two 16-row tiles, N = the block's 16 sequences, K = c),
+//      hi and lo accumulated into the same fp32 tile.
 #include <algorithm>
 
 #include "mla_internal.h"
@@ -24,10 +24,10 @@ namespace mla {
 
 namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kRowsPerWg = 16;  // sequences per work-group (MFMA columns 16..31 unused)
+constexpr int kRowsPerWg = 16;  // sequences per block (the 16 columns of the MFMA tile)
 constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded (conflict-free b128 reads)
 constexpr int kChunk = 8;             // splits whose partials are loaded together
 }  // namespace
@@ -37,55 +37,58 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
                                                            const float* __restrict__ lse_partial,
                                                            const uint16_t* __restrict__ w_uv,
                                                            uint16_t* __restrict__ out, float* __restrict__ lse_out) {
-  __shared__ __attribute__((aligned(16))) char hi_lds[32 * kPitch];
-  __shared__ __attribute__((aligned(16))) char lo_lds[32 * kPitch];
+  __shared__ __attribute__((aligned(16))) char hi_lds[kRowsPerWg * kPitch];
+  __shared__ __attribute__((aligned(16))) char lo_lds[kRowsPerWg * kPitch];
   const int h = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kh = lane >> 5;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  // W_UV rows of the up-projection (A operand: row v = 32 wave + lane % 32, columns 16 ks + 8 kh .. +7)
-  bf16x8 wa[kDc / 16];
-  {
-    const uint4* wrow = reinterpret_cast<const uint4*>(w_uv + ((int64_t)h * kDv + 32 * wave + (lane & 31)) * kDc + 8 * kh);
-#pragma unroll
-    for (int ks = 0; ks < kDc / 16; ++ks) wa[ks] = __builtin_bit_cast(bf16x8, wrow[2 * ks]);
-  }
-
-  // MFMA columns 16..31 (no sequence) read zero rows (written once; the loop only rewrites rows 0..15)
-  {
-    const int zr = 16 + (tid >> 4), zc = 32 * (tid & 15);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      *reinterpret_cast<uint4*>(hi_lds + zr * kPitch + zc * 2 + 16 * k) = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(lo_lds + zr * kPitch + zc * 2 + 16 * k) = make_uint4(0, 0, 0, 0);
-    }
-  }
-  // blocks of 16 sequences; W_UV stays in registers across them
   const int nblk = (batch + kRowsPerWg - 1) / kRowsPerWg;
-  const int blk_end = min(nblk, (int)(blockIdx.y + 1) * blocks_per_wg);
-  for (int blk = blockIdx.y * blocks_per_wg; blk < blk_end; ++blk) {
+  const int blk_begin = blockIdx.y * blocks_per_wg;
+  const int blk_end = min(nblk, blk_begin + blocks_per_wg);
+  if (blk_begin >= blk_end) return;
+
+  // Merge role: thread t owns sequence b0 + t / 16 and latent columns 32 (t % 16) .. +31 of a block.
+  const int bl = tid >> 4;
+  const int c0 = 32 * (tid & 15);
+  // The first kChunk splits of a block: log-sum-exps and partials issued together, without branches
+  // (an index past the last split reads the last one and gets weight zero).
+  float ls[kChunk];
+  uint4 v[kChunk][4];
+  auto load_first_chunk = [&](int blk) {
+    const int b = blk * kRowsPerWg + bl;
+    const int64_t base = ((int64_t)(b < batch ? b : 0) * n_heads + h) * num_splits;
+#pragma unroll
+    for (int q = 0; q < kChunk; ++q) ls[q] = lse_partial[base + min(q, num_splits - 1)];  // masked at use
+#pragma unroll
+    for (int q = 0; q < kChunk; ++q) {
+      const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(q, num_splits - 1)) * kDc + c0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[q][k] = src[k];
+    }
+  };
+
+  // W_UV rows of the up-projection (A operand of tile vt: row v = 32 wave + 16 vt + lane % 16,
+  // columns 32 ks + 8 (lane / 16) .. +7), kept in registers across blocks
+  bf16x8 wa[2][kDc / 32];
+  auto load_wuv = [&]() {
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) {
+      const uint4* wrow = reinterpret_cast<const uint4*>(
+          w_uv + ((int64_t)h * kDv + 32 * wave + 16 * vt + (lane & 15)) * kDc + 8 * (lane >> 4));
+#pragma unroll
+      for (int ks = 0; ks < kDc / 32; ++ks) wa[vt][ks] = __builtin_bit_cast(bf16x8, wrow[4 * ks]);
+    }
+  };
+
+  auto process_block = [&](int blk) {
     const int b0 = blk * kRowsPerWg;
-    // ---- 1. merge the splits: thread t owns sequence b0 + t / 16 and latent columns 32 (t % 16) .. +31
+    // ---- 1. merge the splits (fp32) and stage the merged latent as bf16 hi + lo
     {
-      const int bl = tid >> 4;
       const int b = b0 + bl;
       const bool bok = b < batch;
-      const int c0 = 32 * (tid & 15);
       const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
-      // the first kChunk splits: log-sum-exps and partials issued together, without branches (an
-      // index past the last split reads the last one and gets weight zero), so one wait covers them
-      float ls[kChunk];
-      uint4 v[kChunk][4];
 #pragma unroll
-      for (int q = 0; q < kChunk; ++q) {
-        const float l = lse_partial[base + min(q, num_splits - 1)];
-        ls[q] = q < num_splits ? l : -INFINITY;
-      }
-#pragma unroll
-      for (int q = 0; q < kChunk; ++q) {
-        const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(q, num_splits - 1)) * kDc + c0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[q][k] = src[k];
-      }
+      for (int q = 0; q < kChunk; ++q) ls[q] = q < num_splits ? ls[q] : -INFINITY;
       float m = -INFINITY;
 #pragma unroll
       for (int q = 0; q < kChunk; ++q) m = fmaxf(m, ls[q]);
@@ -114,9 +117,9 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
         }
       };
       if (bok && m != -INFINITY) {
+        // an empty split (lse = -inf, zero partial) and an index past the last split get weight 0
 #pragma unroll
-        for (int q = 0; q < kChunk; ++q)  // an empty split (lse = -inf) contributes nothing
-          if (ls[q] != -INFINITY) accumulate(__expf(ls[q] - m) * inv_z, v[q]);
+        for (int q = 0; q < kChunk; ++q) accumulate(ls[q] == -INFINITY ? 0.f : __expf(ls[q] - m) * inv_z, v[q]);
         // further splits, kChunk at a time, every load of a chunk issued before the first multiply-add
         for (int s0 = kChunk; s0 < num_splits; s0 += kChunk) {
 #pragma unroll
@@ -129,8 +132,7 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
             for (int k = 0; k < 4; ++k) v[q][k] = src[k];
           }
 #pragma unroll
-          for (int q = 0; q < kChunk; ++q)
-            if (ls[q] != -INFINITY) accumulate(__expf(ls[q] - m) * inv_z, v[q]);
+          for (int q = 0; q < kChunk; ++q) accumulate(ls[q] == -INFINITY ? 0.f : __expf(ls[q] - m) * inv_z, v[q]);
         }
       }
       char* hrow = hi_lds + bl * kPitch + c0 * 2;
@@ -140,11 +142,9 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const uint16_t h0 = f32_to_bf16(acc[k + e]), h1 = f32_to_bf16(acc[k + e + 1]);
-          const uint16_t l0 = f32_to_bf16(acc[k + e] - bf16_to_f32(h0));
-          const uint16_t l1 = f32_to_bf16(acc[k + e + 1] - bf16_to_f32(h1));
-          hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          hw[e / 2] = pack_bf16x2(acc[k + e], acc[k + e + 1]);
+          lw[e / 2] = pack_bf16x2(acc[k + e] - __uint_as_float(hw[e / 2] << 16),
+                                  acc[k + e + 1] - __uint_as_float(hw[e / 2] & 0xFFFF0000u));
         }
         *reinterpret_cast<uint4*>(hrow + k * 2) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         *reinterpret_cast<uint4*>(lrow + k * 2) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -152,30 +152,43 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
     }
     __syncthreads();
 
-    // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32): A = W_UV rows (registers), B = merged latent (LDS)
-    const int b = b0 + (lane & 31);
-    const bool bok = (lane & 31) < kRowsPerWg && b < batch;
-    const lds_char* hb = (lds_char*)hi_lds + (lane & 31) * kPitch + 16 * kh;
-    const lds_char* lb = (lds_char*)lo_lds + (lane & 31) * kPitch + 16 * kh;
-    f32x16 acc = f32x16{};
+    // ---- 2. out^T[v, b] for v in [32 wave, 32 wave + 32) (tiles vt) and the block's 16 sequences:
+    // A = W_UV rows (registers), B = merged latent (LDS, lane: sequence lane % 16, columns 32 ks + 8 (lane / 16))
+    {
+      const lds_char* hb = (lds_char*)hi_lds + (lane & 15) * kPitch + 16 * (lane >> 4);
+      const lds_char* lb = (lds_char*)lo_lds + (lane & 15) * kPitch + 16 * (lane >> 4);
+      f32x4 acc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int ks = 0; ks < kDc / 16; ++ks) {
-      const bf16x8 bh = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(hb + 32 * ks);
-      const bf16x8 bl = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lb + 32 * ks);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bh, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks], bl, acc, 0, 0, 0);
-    }
-    // D: lane holds sequence b (column) and output dims 32 wave + 8 q + 4 kh + (0..3)
-    if (bok) {
-      uint16_t* dst = out + ((int64_t)b * n_heads + h) * kDv + 32 * wave;
+      for (int ks = 0; ks < kDc / 32; ++ks) {
+        const bf16x8 bh = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(hb + 64 * ks);
+        const bf16x8 bq = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lb + 64 * ks);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w0 = (uint32_t)f32_to_bf16(acc[4 * q]) | ((uint32_t)f32_to_bf16(acc[4 * q + 1]) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16(acc[4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[4 * q + 3]) << 16);
-        *reinterpret_cast<uint2*>(dst + 8 * q + 4 * kh) = make_uint2(w0, w1);
+        for (int vt = 0; vt < 2; ++vt) {
+          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], bh, acc[vt], 0, 0, 0);
+          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], bq, acc[vt], 0, 0, 0);
+        }
+      }
+      // D of tile vt: lane holds sequence b0 + lane % 16 and output dims 32 wave + 16 vt + 4 (lane / 16) + (0..3)
+      const int b = b0 + (lane & 15);
+      if (b < batch) {
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+          uint16_t* dst = out + ((int64_t)b * n_heads + h) * kDv + 32 * wave + 16 * vt + 4 * (lane >> 4);
+          *reinterpret_cast<uint2*>(dst) =
+              make_uint2(pack_bf16x2(acc[vt][0], acc[vt][1]), pack_bf16x2(acc[vt][2], acc[vt][3]));
+        }
       }
     }
     __syncthreads();  // the next block rewrites the merged rows
+  };
+
+  // First block: its partials go out first, W_UV behind them, so the merge runs while W_UV arrives.
+  load_first_chunk(blk_begin);
+  load_wuv();
+  process_block(blk_begin);
+  for (int blk = blk_begin + 1; blk < blk_end; ++blk) {
+    load_first_chunk(blk);
+    process_block(blk);
   }
 }
 

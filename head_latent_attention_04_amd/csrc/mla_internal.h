@@ -32,6 +32,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// two floats -> packed bf16 pair (low half = a), round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 // double -> bf16, round to nearest even: first to float rounding toward zero with a sticky
 // low bit (round-to-odd), which keeps the exact tie information, then float -> bf16 RNE.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
