@@ -406,7 +406,8 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     for (int i = threadIdx.x; i < kStageBytes / 16; i += kWaves * 64)
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (kStages - 1) * kStageBytes + 16 * i) = z;
   }
-  constexpr int kHalfPv = 4 * HT;  // reduction MFMAs interleaved with the scores; the rest go with the softmax
+  constexpr int kScorePv = 4 * HT;            // reduction MFMAs interleaved with the scores
+  constexpr int kSoftPv = 8 * HT - kScorePv;  // the rest, spread over the softmax
   uint32_t pw[8];
   for (int k = 0; k < nstages; ++k) {
     // stage k has landed once only the stage issued after it (if any) is outstanding
@@ -446,7 +447,7 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
         else
           score_mfma(sacc, a, qreg[ks]);
 #pragma unroll
-        for (int i = ks * kHalfPv / 36; i < (ks + 1) * kHalfPv / 36; ++i) pv_mfma(stp, pp, i);
+        for (int i = ks * kScorePv / 36; i < (ks + 1) * kScorePv / 36; ++i) pv_mfma(stp, pp, i);
         if ((ks & 3) == 1 && copy_next) stage_copy_band(cp, ks >> 2);
         // keep this order: the scheduler would otherwise hoist operand loads and run out of registers
         __builtin_amdgcn_sched_barrier(0);
@@ -457,7 +458,7 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     // of stage k-1's reduction runs on the matrix cores meanwhile (12 slots).
     auto pv_slot = [&](int slot) {
 #pragma unroll
-      for (int i = kHalfPv + slot * kHalfPv / 12; i < kHalfPv + (slot + 1) * kHalfPv / 12; ++i) pv_mfma(stp, pp, i);
+      for (int i = kScorePv + slot * kSoftPv / 12; i < kScorePv + (slot + 1) * kSoftPv / 12; ++i) pv_mfma(stp, pp, i);
       __builtin_amdgcn_sched_barrier(0);
     };
     if (valid < kStageTok) {  // only the split's last, partly filled stage needs a mask
