@@ -69,14 +69,20 @@ def measured_traffic(per_launch_units: str):
     return t.get("bytes_per_launch")
 
 
-def time_loop(torch, fn, n):
+def time_loop(torch, fn, n, host=None):
+    """Average GPU time per call of back-to-back calls; `host` (a dict) receives the host time per
+    call spent enqueueing them."""
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
+    t0 = time.perf_counter()
     for i in range(n):
         fn(i)
+    t1 = time.perf_counter()
     e1.record(s)
     e1.synchronize()
+    if host is not None:
+        host["us_per_call"] = (t1 - t0) * 1e6 / n
     return e0.elapsed_time(e1) / n
 
 
@@ -194,7 +200,8 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ms_step_eager = time_loop(torch, step, args.steps)
+    host = {}
+    ms_step_eager = time_loop(torch, step, args.steps, host)
 
     # The same step as a HIP graph of the four launches (one graph per input set), replayed: reported
     # beside the eager step (the gaps between dependent kernels stay on the device either way).
@@ -253,6 +260,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "ms_per_step_graph_replay": round(ms_step_graph, 5),
+        "host_enqueue_us_per_step": round(host["us_per_call"], 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -25,6 +25,8 @@
 //     the accumulators are never rescaled in the loop.
 //   * The split's normalised latent partial (bf16) is staged in LDS and written as whole 1 KB rows,
 //     its log-sum-exp (fp32) beside it; a separate kernel merges splits.
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -136,6 +138,16 @@ __device__ __forceinline__ void issue_stage(const uint16_t* src_blk, int half, u
   const StageCopy c = stage_copy(src_blk, half, lds_stage, valid, wave, lane);
 #pragma unroll
   for (int band = 0; band < kBands; ++band) stage_copy_band(c, band);
+}
+
+// for (I = B; I < E; ++I) f(I) with I a compile-time constant in every call: the register arrays the
+// body indexes (queries, accumulators, operands) stay in registers whatever the unroller decides.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Work-group barrier without the memory fence of __syncthreads(): that fence would also wait for
@@ -420,12 +432,11 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     const lds_char* stp = lds + ((k + kStages - 1) % kStages) * kStageBytes;  // stage k-1
     const lds_char* pp = pl + ((k + 1) & 1) * kPBytes;                        // P(k-1)
     const bool copy_next = k + 2 < nstages;
-    StageCopy cp;
-    if (copy_next) {
-      const int kn = k + 2;
-      cp = stage_copy(block_ptr(cache, b, blk0 + (kn >> 1)), kn & 1, lds0 + (kn % kStages) * kStageBytes,
-                      min(kStageTok, t1 - t0 - kn * kStageTok), wave, lane);
-    }
+    // descriptor of stage k+2's copy, formed on every step (for a stage past the end it names the
+    // split's last stage and is not issued), so it stays wave-uniform, in scalar registers
+    const int kn = min(k + 2, nstages - 1);
+    const StageCopy cp = stage_copy(block_ptr(cache, b, blk0 + (kn >> 1)), kn & 1, lds0 + (kn % kStages) * kStageBytes,
+                                    min(kStageTok, t1 - t0 - kn * kStageTok), wave, lane);
 
     // every wave runs this body; a wave without a head tile scores a duplicate and drops it
     const int valid = min(kStageTok, t1 - t0 - k * kStageTok);
@@ -437,30 +448,36 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
       bf16x8 a_buf[kAhead];
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) a_buf[i] = lds_b128(st + qk_base[i & 3] + (i >> 2) * 1024);
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
+      static_for<0, 36>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
         const bf16x8 a = a_buf[ks % kAhead];
-        const int kn = ks + kAhead;
-        if (kn < 36) a_buf[ks % kAhead] = lds_b128(st + qk_base[kn & 3] + (kn >> 2) * 1024);
-        if (ks == 0)
+        constexpr int kn = ks + kAhead;
+        if constexpr (kn < 36) a_buf[ks % kAhead] = lds_b128(st + qk_base[kn & 3] + (kn >> 2) * 1024);
+        if constexpr (ks == 0)
           score_mfma_first(sacc, a, qreg[0]);
         else
           score_mfma(sacc, a, qreg[ks]);
-#pragma unroll
-        for (int i = ks * kScorePv / 36; i < (ks + 1) * kScorePv / 36; ++i) pv_mfma(stp, pp, i);
-        if ((ks & 3) == 1 && copy_next) stage_copy_band(cp, ks >> 2);
+        static_for<ks * kScorePv / 36, (ks + 1) * kScorePv / 36>([&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
+        if constexpr ((ks & 3) == 1) {
+          if (copy_next) stage_copy_band(cp, ks >> 2);
+        }
         // keep this order: the scheduler would otherwise hoist operand loads and run out of registers
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     }
     score_mfma_drain(sacc);
     // ---- softmax weights; element j is token 8*(j>>2) + 4*kh + (j&3) of the stage. The other half
     // of stage k-1's reduction runs on the matrix cores meanwhile (12 slots).
-    auto pv_slot = [&](int slot) {
-#pragma unroll
-      for (int i = kScorePv + slot * kSoftPv / 12; i < kScorePv + (slot + 1) * kSoftPv / 12; ++i) pv_mfma(stp, pp, i);
+    auto pv_slot = [&](auto SLOT) {
+      constexpr int slot = decltype(SLOT)::value;
+      static_for<kScorePv + slot * kSoftPv / 12, kScorePv + (slot + 1) * kSoftPv / 12>(
+          [&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
       __builtin_amdgcn_sched_barrier(0);
     };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S11 = std::integral_constant<int, 11>;
     if (valid < kStageTok) {  // only the split's last, partly filled stage needs a mask
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -468,26 +485,26 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
         if (tk >= valid) sacc[j] = -INFINITY;
       }
     }
-    pv_slot(0);
+    pv_slot(S0{});
     float mx = sacc[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
-    pv_slot(1);
+    pv_slot(S1{});
     mx = pair_max(mx) * scale_log2;  // scale > 0: the max commutes with it
     if (m_ref == -INFINITY) m_ref = mx;
     overflow |= mx > m_ref + kMaxExcess;
-    pv_slot(2);
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
+    pv_slot(S2{});
+    static_for<0, 8>([&](auto JJ) {
+      constexpr int j = 2 * decltype(JJ)::value;
       // raw v_exp_f32: weights below 2^-126 flush to zero, which a softmax weight can afford
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], scale_log2, -m_ref));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], scale_log2, -m_ref));
       lsum += p0 + p1;
       pw[j >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
       asm volatile("" ::"v"(pw[j >> 1]));  // computed here, between the reduction MFMAs, not sunk to its store
-      pv_slot(3 + (j >> 1));
-    }
-    pv_slot(11);
+      pv_slot(std::integral_constant<int, 3 + (j >> 1)>{});
+    });
+    pv_slot(S11{});
     if (qk_wave) {  // P(k)[head][tokens 8 q + 4 kh .. +3] <- (pw[2q], pw[2q+1]), into the other buffer
       const int ps = p_swz(n);
       lds_char* pk = pl + (k & 1) * kPBytes;
