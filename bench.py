@@ -221,14 +221,16 @@ def main():
     ms_step_graph = time_loop(torch, lambda i: graphs[i % nsets].replay(), args.steps)
     ms_step = ms_step_eager
 
-    # each kernel of the step alone, per launch (the absorbed queries of every set are in place), and
-    # the standalone RoPE + append and absorption kernels the fused front half replaces
+    # each kernel of the step alone: N launches back to back on the launch stream between one pair of
+    # events, rotating the input sets (the absorbed queries of every set are in place); the average
+    # per launch includes the gap to the next launch. Also the standalone RoPE + append and
+    # absorption kernels the fused front half replaces.
     ms = {}
     for name, fn in (("rope_append_absorb", front), ("decode_attention", attend), ("combine_wuv", comb),
                      ("rope_append_alone", rope), ("absorb_alone", absorb)):
         for i in range(args.warmup):
             fn(i)
-        ms[name] = time_each(torch, fn, args.steps)
+        ms[name] = time_loop(torch, fn, args.steps)
     ms_attn = ms["decode_attention"]
 
     # a plain device copy of known size: the achievable-bandwidth context for the roofline, and the

@@ -241,16 +241,19 @@ __device__ __forceinline__ void exact_head_fallback(const CacheView& cache, int 
 
 }  // namespace
 
-// HT: head tiles of 32 per work-group (1..4); kOperandOrder: layout of q_abs (see mla_internal.h).
+template <int HT>
+constexpr int kPBytesOf = HT * 32 * kPHeadBytes;  // weights P of one stage
+
+// The work of one attention work-group (blockIdx.x: its logical block). HT: head tiles of 32 per
+// work-group (1..4); kOperandOrder: layout of q_abs (see mla_internal.h). smem_raw: the stage
+// buffers (kStages * kStageBytes, 1 KB aligned); p_raw: P of two stages (2 * kPBytesOf<HT>).
 template <int HT, bool kOperandOrder>
-__global__ void __launch_bounds__(kWaves * 64, 1)
-decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __restrict__ seq_lens,
-                   const int32_t* __restrict__ cu_q_lens, int batch, const uint16_t* __restrict__ q_abs,
-                   float scale_log2, int split_tokens, int num_splits, uint16_t* __restrict__ o_partial,
-                   float* __restrict__ lse_partial) {
-  constexpr int kPBytes = HT * 32 * kPHeadBytes;  // weights P of one stage
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) char p_raw[2 * kPBytes];  // P of two stages
+__device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads, int n_groups,
+                                            const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q_lens,
+                                            int batch, const uint16_t* __restrict__ q_abs, float scale_log2,
+                                            int split_tokens, int num_splits, uint16_t* __restrict__ o_partial,
+                                            float* __restrict__ lse_partial, char* smem_raw, char* p_raw) {
+  constexpr int kPBytes = kPBytesOf<HT>;
   lds_char* lds = (lds_char*)smem_raw;
   lds_char* pl = (lds_char*)p_raw;
 
@@ -576,6 +579,19 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
     }
   }
 }
+
+template <int HT, bool kOperandOrder>
+__global__ void __launch_bounds__(kWaves * 64, 1)
+decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __restrict__ seq_lens,
+                   const int32_t* __restrict__ cu_q_lens, int batch, const uint16_t* __restrict__ q_abs,
+                   float scale_log2, int split_tokens, int num_splits, uint16_t* __restrict__ o_partial,
+                   float* __restrict__ lse_partial) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char p_raw[2 * kPBytesOf<HT>];
+  attend_tile<HT, kOperandOrder>(cache, n_heads, n_groups, seq_lens, cu_q_lens, batch, q_abs, scale_log2, split_tokens,
+                                 num_splits, o_partial, lse_partial, smem_raw, p_raw);
+}
+
 
 template <int HT, bool kOperandOrder>
 static hipError_t launch_ht(const CacheView& cache, int rows, int n_heads, const int32_t* seq_lens,
