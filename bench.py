@@ -377,7 +377,7 @@ def prefill_main(args, torch, lib, props):
                                f"latent cache", "total_q": total_q, "n_heads": H, "d_c": 512, "d_rope": 64,
                    "d_nope": 128, "d_v": 128},
         "kernels_ms": {k: round(v, 4) for k, v in ms.items()},
-        "roofline": {"kernel": "mla_chunked_prefill (absorb + decode_mfma_kernel<4, true> causal rows + combine)",
+        "roofline": {"kernel": "mla_chunked_prefill (absorb + decode_mfma_kernel<4, false> causal rows + combine)",
                      "bound": "mfma", "achieved": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

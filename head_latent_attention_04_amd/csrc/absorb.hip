@@ -41,7 +41,11 @@ __device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
 constexpr int kAbsorbLds = kDnope * kPitch;  // bytes of LDS one absorption work-group uses
 
 // Work-group (head h, column half ch, rows rbase .. rbase + rows_per_wg - 1). q_rope == nullptr: the
-// RoPE part of the rows is written by someone else (the fused RoPE work-groups).
+// RoPE part of the rows is written by someone else (the fused RoPE work-groups). kPlain: write the
+// rows as plain [rows, n_heads, 576] (whole 16-byte runs of one row per lane pair, so a work-group
+// fills whole lines: the layout for many rows) instead of the attention kernel's operand order
+// (whose lines mix 32 heads, so a work-group writes 16-byte pieces of lines other work-groups share).
+template <bool kPlain>
 __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, int n_heads, int rows_per_wg,
                                             const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
                                             const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs,
@@ -50,12 +54,18 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
   const int tiles = q_tiles(n_heads);
   lds_char* lds = (lds_char*)w_lds;
 
+  // element (r, d) of this head in the output layout
+  auto out_off = [&](int64_t r, int d) -> int64_t {
+    if constexpr (kPlain) return (r * n_heads + h) * kRow + d;
+    return q_perm_offset(r, tiles, h, d);
+  };
   if (h >= n_heads) {  // padding head of the last tile: zero query (columns of this half, RoPE part in half 0)
+    if constexpr (kPlain) return;  // no padding heads in the plain layout
     const int cols = ch == 0 ? kCols + kDr : kCols;
     for (int i = tid; i < rows_per_wg * (cols / 8); i += 256) {
       const int r = rbase + i / (cols / 8), c8 = i % (cols / 8);
       const int d = c8 * 8 < kCols ? ch * kCols + c8 * 8 : kDc + (c8 * 8 - kCols);
-      if (r < rows) *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, d)) = make_uint4(0, 0, 0, 0);
+      if (r < rows) *reinterpret_cast<uint4*>(q_abs + out_off(r, d)) = make_uint4(0, 0, 0, 0);
     }
     return;
   }
@@ -92,7 +102,7 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
     for (int i = tid; i < rows_per_wg * (kDr / 8); i += 256) {
       const int r = rbase + i / (kDr / 8), c8 = i % (kDr / 8);
       if (r < rows)
-        *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, kDc + 8 * c8)) =
+        *reinterpret_cast<uint4*>(q_abs + out_off(r, kDc + 8 * c8)) =
             reinterpret_cast<const uint4*>(q_rope + ((int64_t)r * n_heads + h) * kDr)[c8];
     }
   }
@@ -136,7 +146,7 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
         const uint4 v = kh == 0 ? make_uint4(w[2 * q], w[2 * q + 1], t0, t1)
                                 : make_uint4(t0, t1, w[2 * q + 2], w[2 * q + 3]);
         const int d = ch * kCols + cb + 8 * (q + kh);
-        if (r < rows) *reinterpret_cast<uint4*>(q_abs + q_perm_offset(r, tiles, h, d)) = v;
+        if (r < rows) *reinterpret_cast<uint4*>(q_abs + out_off(r, d)) = v;
       }
     }
 #pragma unroll
@@ -144,14 +154,15 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
   }
 }
 
+template <bool kPlain>
 __global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, int rows_per_wg,
                                                           const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           uint16_t* __restrict__ q_abs) {
   __shared__ __attribute__((aligned(16))) char w_lds[kAbsorbLds];
-  absorb_tile(blockIdx.x, blockIdx.y, blockIdx.z * rows_per_wg, rows, n_heads, rows_per_wg, q_nope, q_rope, w_uk, q_abs,
-              w_lds);
+  absorb_tile<kPlain>(blockIdx.x, blockIdx.y, blockIdx.z * rows_per_wg, rows, n_heads, rows_per_wg, q_nope, q_rope, w_uk,
+                      q_abs, w_lds);
 }
 
 // RoPE + append and absorption in one launch: the first n_rope work-groups are (token, head group)
@@ -175,7 +186,7 @@ __global__ void __launch_bounds__(256) rope_absorb_kernel(CacheView cache, int n
   }
   const int hp = 32 * tiles;
   const int a = blockIdx.x - n_rope;
-  absorb_tile(a % hp, (a / hp) % (kDc / kCols), (a / (hp * (kDc / kCols))) * rows_per_wg, rows, n_heads, rows_per_wg,
+  absorb_tile<false>(a % hp, (a / hp) % (kDc / kCols), (a / (hp * (kDc / kCols))) * rows_per_wg, rows, n_heads, rows_per_wg,
               q_nope, nullptr, w_uk, q_abs, smem);
 }
 
@@ -191,14 +202,18 @@ int absorb_rows_per_wg(int rows, int n_heads) {
 }  // namespace
 
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
-                         const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream) {
+                         const uint16_t* w_uk, uint16_t* q_abs, bool plain, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int hp = 32 * q_tiles(n_heads);
   const int rows_per_wg = absorb_rows_per_wg(rows, n_heads);
   const int zb = (rows + rows_per_wg - 1) / rows_per_wg;
   if (zb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads, rows_per_wg,
-                     q_nope, q_rope, w_uk, q_abs);
+  if (plain)
+    hipLaunchKernelGGL(absorb_mfma_kernel<true>, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads,
+                       rows_per_wg, q_nope, q_rope, w_uk, q_abs);
+  else
+    hipLaunchKernelGGL(absorb_mfma_kernel<false>, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads,
+                       rows_per_wg, q_nope, q_rope, w_uk, q_abs);
   return hipGetLastError();
 }
 

@@ -29,9 +29,12 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kRowsPerWg = 16;  // sequences per block (the 16 columns of the MFMA tile)
 constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded (conflict-free b128 reads)
-constexpr int kChunk = 8;             // splits whose partials are loaded together
 }  // namespace
 
+// kChunk: splits whose partials are loaded together (1, 2, 4 or 8: the split count rounded up to a
+// power of two, at most 8). With kChunk <= 2 the next block's partials are loaded while the current
+// block is merged and projected, which matters when a work-group runs many blocks (prefill, S = 1).
+template <int kChunk>
 __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_heads, int num_splits, int blocks_per_wg,
                                                            const uint16_t* __restrict__ o_partial,
                                                            const float* __restrict__ lse_partial,
@@ -52,9 +55,10 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
   const int c0 = 32 * (tid & 15);
   // The first kChunk splits of a block: log-sum-exps and partials issued together, without branches
   // (an index past the last split reads the last one and gets weight zero).
-  float ls[kChunk];
-  uint4 v[kChunk][4];
-  auto load_first_chunk = [&](int blk) {
+  constexpr bool kPrefetch = kChunk <= 2;
+  float ls[kChunk], ls_next[kChunk];
+  uint4 v[kChunk][4], v_next[kChunk][4];
+  auto load_first_chunk = [&](int blk, float (&ls)[kChunk], uint4 (&v)[kChunk][4]) {
     const int b = blk * kRowsPerWg + bl;
     const int64_t base = ((int64_t)(b < batch ? b : 0) * n_heads + h) * num_splits;
 #pragma unroll
@@ -183,11 +187,24 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
   };
 
   // First block: its partials go out first, W_UV behind them, so the merge runs while W_UV arrives.
-  load_first_chunk(blk_begin);
+  load_first_chunk(blk_begin, ls, v);
   load_wuv();
-  process_block(blk_begin);
-  for (int blk = blk_begin + 1; blk < blk_end; ++blk) {
-    load_first_chunk(blk);
+  for (int blk = blk_begin; blk < blk_end; ++blk) {
+    if (blk > blk_begin) {
+      if constexpr (kPrefetch) {
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) {
+          ls[q] = ls_next[q];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[q][k] = v_next[q][k];
+        }
+      } else {
+        load_first_chunk(blk, ls, v);
+      }
+    }
+    if constexpr (kPrefetch) {
+      if (blk + 1 < blk_end) load_first_chunk(blk + 1, ls_next, v_next);  // in flight during this block
+    }
     process_block(blk);
   }
 }
@@ -202,8 +219,18 @@ hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t
   const int64_t bpw = std::max<int64_t>(1, (nblk * n_heads + 511) / 512);
   const int64_t yb = (nblk + bpw - 1) / bpw;
   if (yb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_mfma_kernel, dim3(n_heads, (unsigned)yb), dim3(256), 0, stream, batch, n_heads, num_splits,
-                     (int)bpw, o_partial, lse_partial, w_uv, out, lse_out);
+#define MLA_LAUNCH_COMBINE(C_)                                                                                   \
+  hipLaunchKernelGGL(combine_mfma_kernel<C_>, dim3(n_heads, (unsigned)yb), dim3(256), 0, stream, batch, n_heads, \
+                     num_splits, (int)bpw, o_partial, lse_partial, w_uv, out, lse_out)
+  if (num_splits <= 1)
+    MLA_LAUNCH_COMBINE(1);
+  else if (num_splits == 2)
+    MLA_LAUNCH_COMBINE(2);
+  else if (num_splits <= 4)
+    MLA_LAUNCH_COMBINE(4);
+  else
+    MLA_LAUNCH_COMBINE(8);
+#undef MLA_LAUNCH_COMBINE
   return hipGetLastError();
 }
 

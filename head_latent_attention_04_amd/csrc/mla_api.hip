@@ -120,7 +120,7 @@ int mla_absorb(const mla_dims* dims, int32_t rows, const uint16_t* q_nope, const
   if (workspace_bytes < mla_decode_workspace_size(dims, rows)) return MLA_ERR_BAD_ARG;
   if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
   return launched(mla::launch_absorb(rows, dims->n_heads, q_nope, q_rope, w_uk, static_cast<uint16_t*>(workspace),
-                                     stream));
+                                     false, stream));
 }
 
 int mla_rope_append_absorb(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens, const int32_t* token_seq,
@@ -222,12 +222,13 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + lay.q_abs);
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + lay.o_lat);
   float* lse = reinterpret_cast<float*>(ws + lay.lse);
-  hipError_t e = mla::launch_absorb(total_q, dims->n_heads, q_nope, q_rope, w_uk, q_abs, stream);
+  // many rows: the absorbed queries in the plain layout, which the absorption writes in whole lines
+  hipError_t e = mla::launch_absorb(total_q, dims->n_heads, q_nope, q_rope, w_uk, q_abs, true, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   // one query token per row; the whole causal key range of a row is one split (split_tokens is
   // only the split length, so any multiple of the block covering the longest sequence works)
   (void)max_q_len;
-  e = mla::launch_attention(view(cache), total_q, dims->n_heads, seq_lens, cu_q_lens, batch, q_abs, true, dims->scale,
+  e = mla::launch_attention(view(cache), total_q, dims->n_heads, seq_lens, cu_q_lens, batch, q_abs, false, dims->scale,
                             kMaxSplitTokens, 1, o_lat, lse, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   return launched(mla::launch_combine(total_q, dims->n_heads, 1, o_lat, lse, w_uv, out, lse_out, stream));

@@ -75,9 +75,9 @@ hipError_t launch_rope_append(const CacheView& cache, int n_heads, int num_token
                               uint16_t* q_rope, float theta, hipStream_t stream);
 
 // q_abs(r, h, 0:512) = W_UK[h]^T q_nope[r, h]; q_abs(r, h, 512:576) = q_rope[r, h] (bf16), r < rows,
-// written in the operand-order layout above (padding heads zero).
+// written in the operand-order layout above (padding heads zero), or, if plain, as [rows, n_heads, 576].
 hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const uint16_t* q_rope,
-                         const uint16_t* w_uk, uint16_t* q_abs, hipStream_t stream);
+                         const uint16_t* w_uk, uint16_t* q_abs, bool plain, hipStream_t stream);
 
 // launch_rope_append (with the query) and launch_absorb of the same num_tokens rows in one launch:
 // row i of q_abs is token i, its RoPE part the query launch_rope_append rotates in place.
