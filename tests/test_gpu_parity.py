@@ -67,6 +67,7 @@ SMALL = [
     ("h48_L300_contig_st128", 48, [300], False, 128),
     ("h128_L4096x2_planned", 128, [4096, 4096], False, None),
     ("h64_L577_one_split", 64, [577, 130], True, 640),
+    ("h272_two_head_groups_st128", 272, [500, 129, 1], True, 128),  # 3 work-group head groups, last partial
 ]
 
 
@@ -189,7 +190,8 @@ def test_empty_sequence_and_poisoned_tail():
     assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
 
 
-@pytest.mark.parametrize("H,lens,qlens", [(16, [70, 33], [40, 33]), (32, [200, 1], [65, 1]), (128, [130], [130])])
+@pytest.mark.parametrize("H,lens,qlens", [(16, [70, 33], [40, 33]), (32, [200, 1], [65, 1]), (128, [130], [130]),
+                                          (160, [90, 40], [20, 40])])
 def test_prefill_matches_oracle(H, lens, qlens):
     say(f"[prefill] H={H} lens={lens} q={qlens}")
     case = make_case("prefill", 61, H, lens, q_lens=qlens, paged=True, spare_blocks=2)
