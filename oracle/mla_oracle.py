@@ -37,6 +37,8 @@ Readings where the pages leave a step open (each is also listed in the design no
     keys 0..L-1. Prefill: query at position p sees keys 0..p (causal).
   * lse is the natural-log log-sum-exp of the scaled scores.
   * bf16 rounding is round-to-nearest-even.
+  * KV down-projection: wkv_a's output is rounded to bf16 before the split (the Linear's output
+    dtype); RMSNorm is computed in float64 with the caller's eps and rounded once.
 """
 from __future__ import annotations
 
@@ -154,6 +156,45 @@ def rope_append(cache: np.ndarray, block_table, max_blocks: int, token_seq, toke
     if q_rope is not None:
         q_rot = f64_to_bf16(rope_rotate(bf16_to_f64(q_rope), np.asarray(token_pos)[:, None], theta))
     return cache, q_rot
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gamma over the last axis, float64.
+    ([P1] section 2: kv_norm = RMSNorm(kv_lora_rank) on the latent part of wkv_a's output;
+    section 4: the RMSNorm sits right after the W_DKV projection.)
+    """
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(gamma, np.float64)
+
+
+def kv_split(kv: np.ndarray, d_c: int):
+    """The split of wkv_a's output into the latent part and the decoupled RoPE key ([P1] section 2:
+    kv_latent, k_rope = split(kv_combined, [kv_lora_rank, qk_rope_head_dim]))."""
+    return kv[..., :d_c], kv[..., d_c:]
+
+
+def kv_down(x: np.ndarray, w_dkv: np.ndarray, gamma: np.ndarray, eps: float):
+    """KV down-projection of new tokens, the step ahead of the append ([P1] section 2 forward:
+    kv_combined = wkv_a(x); kv_latent, k_rope = split; kv_latent = kv_norm(kv_latent)).
+
+    x [T, dim], w_dkv [d_c + d_R, dim] (the nn.Linear row layout of wkv_a), gamma [d_c] (kv_norm's
+    weight): bf16 bit patterns. The projection's output is rounded to bf16 (the Linear's output
+    dtype); the latent part is then normalised in float64 and rounded once more.
+    Returns (c_kv [T, d_c], k_rope [T, d_R]) as bf16 bit patterns; k_rope is not rotated yet.
+    """
+    d_c = np.asarray(gamma).shape[0]
+    kv = f64_to_bf16(bf16_to_f64(x) @ bf16_to_f64(w_dkv).T)
+    latent, k_rope = kv_split(kv, d_c)
+    c = f64_to_bf16(rms_norm(bf16_to_f64(latent), bf16_to_f64(gamma), eps))
+    return c, k_rope
+
+
+def kv_down_append(cache: np.ndarray, block_table, max_blocks: int, token_seq, token_pos, x, w_dkv, gamma,
+                   eps: float, theta: float = ROPE_THETA) -> np.ndarray:
+    """kv_down followed by rope_append of the resulting rows; returns the updated cache copy."""
+    c, kr = kv_down(x, w_dkv, gamma, eps)
+    cache, _ = rope_append(cache, block_table, max_blocks, token_seq, token_pos, c, kr, None, theta)
+    return cache
 
 
 def gather_rows(cache: np.ndarray, block_table, max_blocks: int, seq: int, length: int) -> np.ndarray:

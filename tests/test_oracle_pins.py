@@ -338,9 +338,53 @@ def pin_closed_forms():
     assert O.decode_flops_per_token(128, 512, 64) == 278528
 
 
+def pin_rms_norm():
+    # closed form: x = [3, 4] has mean square 12.5; with gamma = [1, 2] and eps = 0 the result is
+    # [3, 8] / sqrt(12.5) = [0.848528137..., 2.262741699...]
+    got = O.rms_norm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 0.0)
+    assert np.allclose(got, [0.8485281374238570, 2.2627416997969520], rtol=0, atol=1e-13)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 512))
+    one = np.ones(512)
+    y = O.rms_norm(x, one, 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=0, atol=1e-12)  # unit RMS
+    assert np.allclose(O.rms_norm(3.7 * x, one, 0.0), y, rtol=0, atol=1e-12)      # scale invariance
+    g = rng.standard_normal(512)
+    assert np.allclose(O.rms_norm(x, g, 0.0), y * g, rtol=0, atol=1e-12)           # weight per column
+    assert np.all(O.rms_norm(np.zeros((1, 512)), one, 1e-6) == 0.0)                 # eps keeps zero finite
+    # eps enters under the root: a row of ones gives 1 / sqrt(1 + eps)
+    assert np.allclose(O.rms_norm(np.ones((1, 8)), np.ones(8), 0.25), 1.0 / math.sqrt(1.25), rtol=0, atol=1e-15)
+
+
+def pin_kv_down():
+    # with w_dkv rows that pick single input columns, the projection is exact: the latent part is
+    # the picked columns (normalised), the RoPE key the rest, in wkv_a's split order
+    rng = np.random.default_rng(6)
+    d_c, d_r, dim, T = 8, 4, 16, 3
+    x = bf16_bits(rng.standard_normal((T, dim)))
+    pick = rng.permutation(dim)[: d_c + d_r]
+    w = np.zeros((d_c + d_r, dim))
+    w[np.arange(d_c + d_r), pick] = 1.0
+    gamma = bf16_bits(1.0 + 0.25 * rng.standard_normal(d_c))
+    c, kr = O.kv_down(x, bf16_bits(w), gamma, 1e-6)
+    xf = O.bf16_to_f64(x)
+    assert np.array_equal(kr, x[:, pick[d_c:]])
+    lat = xf[:, pick[:d_c]]
+    want = lat / np.sqrt((lat * lat).sum(axis=1, keepdims=True) / d_c + 1e-6) * O.bf16_to_f64(gamma)
+    assert np.array_equal(c, O.f64_to_bf16(want))
+    # and the append places [c | R_pos kR] in the slot
+    cache0 = np.zeros((4, 4, d_c + d_r), np.uint16)  # 2 sequences x 2 blocks of 4 rows
+    cache = O.kv_down_append(cache0, None, 2, [1, 0, 1], [5, 2, 0], x, bf16_bits(w), gamma, 1e-6)
+    for i, (b, p) in enumerate([(1, 5), (0, 2), (1, 0)]):
+        assert np.array_equal(cache[b * 2 + p // 4, p % 4, :d_c], c[i])
+        rot = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(kr[i:i + 1]), np.array([p]))[0])
+        assert np.array_equal(cache[b * 2 + p // 4, p % 4, d_c:], rot)
+
+
 PINS = [pin_bf16_rounding, pin_rope_complex_form, pin_rope_invariants, pin_bruteforce_decode,
         pin_bruteforce_prefill, pin_absorbed_equals_expanded, pin_special_cases, pin_wuk_zero_matches_sdpa,
-        pin_split_invariance, pin_prefill_equals_decodes, pin_slot_mapping, pin_closed_forms]
+        pin_split_invariance, pin_prefill_equals_decodes, pin_slot_mapping, pin_closed_forms, pin_rms_norm,
+        pin_kv_down]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -414,7 +458,18 @@ def _mut_round_truncate(monkeypatch):
                                                       >> 16).astype(np.uint16))
 
 
+def _mut_rms_sum(monkeypatch):
+    monkeypatch.setattr(O, "rms_norm", lambda x, g, eps: np.asarray(x, np.float64) / np.sqrt(
+        np.sum(np.asarray(x, np.float64) ** 2, axis=-1, keepdims=True) + eps) * np.asarray(g, np.float64))
+
+
+def _mut_kv_split_swapped(monkeypatch):
+    monkeypatch.setattr(O, "kv_split", lambda kv, d_c: (kv[..., kv.shape[-1] - d_c:], kv[..., :kv.shape[-1] - d_c]))
+
+
 MUTANTS = [
+    (_mut_rms_sum, [pin_rms_norm]),
+    (_mut_kv_split_swapped, [pin_kv_down]),
     (_mut_rope_sign, [pin_rope_complex_form]),
     (_mut_rope_half, [pin_rope_complex_form]),
     (_mut_rope_base_dim, [pin_rope_complex_form]),
