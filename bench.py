@@ -45,9 +45,10 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "kv_down"], default="decode",
                     help="decode: B=32, n_h=128, 4K context (the headline); prefill: chunked prefill, 2 x 1024 "
-                         "new tokens after 8192 cached")
+                         "new tokens after 8192 cached; kv_down: KV down-projection + kv_norm + RoPE append of "
+                         "the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096")
     return ap.parse_args()
 
 
@@ -156,6 +157,8 @@ def main():
     props = torch.cuda.get_device_properties(0)
     if args.workload == "prefill":
         return prefill_main(args, torch, lib, props)
+    if args.workload == "kv_down":
+        return kv_down_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -386,6 +389,112 @@ def prefill_main(args, torch, lib, props):
     }
     if not args.no_cpu:
         result["cpu_baseline"] = prefill_cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+KV_DIM = 4096
+KV_EPS = 1e-6
+
+
+class KvDownSet:
+    """One independent copy of the KV down-projection's inputs and destination on the GPU."""
+
+    def __init__(self, torch, lib, seq_lens, new_lens, seed):
+        from workloads import BF16_NAN, kv_down_layout, make_kv_down_inputs
+        ts, tp, table, nb, mb = kv_down_layout(seq_lens, new_lens, seed)
+        inp = make_kv_down_inputs(seed, len(ts), KV_DIM)
+        dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to("cuda")
+        self.T = len(ts)
+        self.host = (ts, tp, table, nb, mb, inp)
+        self.dims = lib.make_dims(128)
+        self.data = torch.full((nb, 64, 576), int(BF16_NAN), dtype=torch.int16, device="cuda")
+        self.table = dev(table, np.int32)
+        self.cache = lib.make_cache(self.data, self.table, mb)
+        self.ts, self.tp = dev(ts, np.int32), dev(tp, np.int32)
+        self.x, self.w, self.g = dev(inp.x, np.int16), dev(inp.w_dkv, np.int16), dev(inp.gamma, np.int16)
+        self.ws = torch.empty(lib.kv_down_append_workspace_size(self.dims, self.T, KV_DIM), dtype=torch.uint8,
+                              device="cuda")
+
+    def run(self, lib):
+        lib.kv_down_append(self.dims, self.cache, self.ts, self.tp, self.x, self.w, self.g, KV_EPS, self.ws)
+
+
+def kv_down_cpu_baseline(kset, budget_s):
+    """The fp64 oracle's kv_down_append on the 32-token decode append, repeated until the budget is
+    spent; rate in the metric's unit (GB/s of algorithmic bytes)."""
+    from oracle import mla_oracle as O
+    from workloads import BF16_NAN
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    ts, tp, table, nb, mb, inp = kset.host
+    reps = 0
+    t0 = time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < budget_s:
+        cache = np.full((nb, 64, 576), BF16_NAN, np.uint16)
+        O.kv_down_append(cache, table, mb, ts, tp, inp.x, inp.w_dkv, inp.gamma, KV_EPS)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(reps * kv_down_bytes(kset.T) / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{reps} repetitions of the whole {kset.T}-token append, width {KV_DIM}, "
+                                        f"fp64, {dt:.1f} s"}
+
+
+def kv_down_bytes(T):
+    """Algorithmic HBM bytes of one append: W_DKV, x, kv_norm's weight, token ids in; rows out."""
+    return 576 * KV_DIM * 2 + T * KV_DIM * 2 + 512 * 2 + T * 8 + T * 576 * 2
+
+
+def kv_down_main(args, torch, lib, props):
+    # decode step's new tokens: 32 sequences at position 4095; enough copies that the weights do not
+    # stay in the 256 MB Infinity Cache between calls (a model reads a different layer's W_DKV each time)
+    dec = [KvDownSet(torch, lib, [4096] * 32, [1] * 32, 100 + k) for k in range(64)]
+    pre = [KvDownSet(torch, lib, [9216, 9216], [1024, 1024], 200 + k) for k in range(16)]
+    torch.cuda.synchronize()
+    res = {}
+    for name, sets in (("decode", dec), ("prefill", pre)):
+        fn = lambda i, sets=sets: sets[i % len(sets)].run(lib)
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        res[name] = {"back_to_back": time_loop(torch, fn, args.steps), "each": time_each(torch, fn, args.steps)}
+    T_dec, T_pre = dec[0].T, pre[0].T
+    ms_dec, ms_pre = res["decode"]["each"], res["prefill"]["each"]
+    gbps = kv_down_bytes(T_dec) / (ms_dec * 1e-3) / 1e9
+    pre_flops = 2.0 * T_pre * 576 * KV_DIM
+    pre_tflops = pre_flops / (ms_pre * 1e-3) / 1e12
+    result = {
+        "metric": "KV down-projection + kv_norm + RoPE append GB/s, decode step's 32 new tokens, width 4096",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_dec, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"kv_down_append T={T_dec} dim={KV_DIM} (32 sequences at position 4095), paged "
+                               f"bf16 latent cache", "num_tokens": T_dec, "dim": KV_DIM, "d_c": 512, "d_rope": 64,
+                   "input_sets_rotated": len(dec)},
+        "ms_back_to_back": {k: round(v["back_to_back"], 5) for k, v in res.items()},
+        "roofline": {"kernel": "mla_kv_down_append (kv_down_gemm_kernel + kv_down_finish_kernel)", "bound": "hbm",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": kv_down_bytes(T_dec)},
+        "prefill_chunk": {"workload": f"kv_down_append T={T_pre} dim={KV_DIM} (2 x 1024 new after 8192)",
+                          "ms": round(ms_pre, 5), "bound": "mfma", "achieved": round(pre_tflops, 1),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "algorithmic_flop_per_launch": pre_flops, "input_sets_rotated": len(pre)},
+        "device": props.name,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = kv_down_cpu_baseline(dec[0], args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -84,6 +84,29 @@ int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_to
                                           q_rope_inout, dims->rope_theta, stream));
 }
 
+size_t mla_kv_down_append_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim) {
+  if (check_dims(dims) != MLA_OK || num_tokens < 0 || dim <= 0 || dim % 64 != 0) return 0;
+  return mla::kv_down_workspace_bytes(num_tokens, dim);
+}
+
+int mla_kv_down_append(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens, const int32_t* token_seq,
+                       const int32_t* token_pos, const uint16_t* x, int32_t dim, const uint16_t* w_dkv,
+                       const uint16_t* gamma, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535 * 32 || dim <= 0) return MLA_ERR_BAD_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return MLA_ERR_BAD_ARG;
+  if (dim % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MLA_OK;
+  if (!token_seq || !token_pos || !x || !w_dkv || !gamma || !workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < mla::kv_down_workspace_bytes(num_tokens, dim)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0 || ((uintptr_t)x & 15) != 0 || ((uintptr_t)w_dkv & 15) != 0)
+    return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_kv_down(view(cache), num_tokens, token_seq, token_pos, x, dim, w_dkv, gamma, eps,
+                                      dims->rope_theta, workspace, stream));
+}
+
 int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, int32_t num_cus,
                     int32_t* split_tokens, int32_t* num_splits) {
   int st = check_dims(dims);

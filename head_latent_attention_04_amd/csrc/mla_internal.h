@@ -97,6 +97,21 @@ hipError_t launch_attention(const CacheView& cache, int rows, int n_heads, const
                             float scale, int split_tokens, int num_splits, uint16_t* o_partial, float* lse_partial,
                             hipStream_t stream);
 
+// Tiled bf16 GEMM, fp32 partials over K splits: part[s][m][n] = sum_{k in split s} A[m][k] B[n][k].
+// A [M, K], B [N, K] row-major bf16; N % kGemmBN == 0, K % 64 == 0, 1 <= nsplit <= K / 64.
+constexpr int kGemmBM = 128, kGemmBN = 192, kGemmMaxSplits = 16;
+int gemm_bt_splits(int M, int N, int K);
+hipError_t launch_gemm_bt_partial(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
+                                  hipStream_t stream);
+
+// KV down-projection of num_tokens tokens (x [T, dim] . W_DKV^T, W_DKV [576, dim]), RMSNorm of the latent
+// part (eps, weight gamma [512]), then the RoPE rotation of k_R and the append, as launch_rope_append.
+// workspace: kv_down_workspace_bytes(num_tokens, dim) bytes (fp32 split partials).
+size_t kv_down_workspace_bytes(int num_tokens, int dim);
+hipError_t launch_kv_down(const CacheView& cache, int num_tokens, const int32_t* token_seq, const int32_t* token_pos,
+                          const uint16_t* x, int dim, const uint16_t* w_dkv, const uint16_t* gamma, float eps,
+                          float theta, void* workspace, hipStream_t stream);
+
 // LSE merge over splits + W_UV up-projection.
 hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t* o_partial,
                           const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,

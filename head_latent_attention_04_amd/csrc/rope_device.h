@@ -21,6 +21,20 @@ constexpr int kRopeHeadsPerGroup = 32;  // heads per work-group: 8 threads per h
 
 __host__ __device__ inline int rope_groups(int n_heads) { return (n_heads + kRopeHeadsPerGroup - 1) / kRopeHeadsPerGroup; }
 
+// cos and sin of pair j's angle at position pos: theta_j = base^(-2j/d_R), formed as exp2 of an
+// exactly representable multiple of log2(base), turned in fp64.
+__device__ __forceinline__ void rope_cos_sin(int pos, int j, double log2_theta, double* c, double* s) {
+  const double inv = exp2(-(2.0 * j / kDr) * log2_theta);
+  sincos((double)pos * inv, s, c);
+}
+
+// One interleaved pair (x_2j in the low half, x_2j+1 in the high half of w) turned by (c, s), each
+// result rounded once to bf16.
+__device__ __forceinline__ uint32_t rope_turn_pair(uint32_t w, double c, double s) {
+  const double x0 = bf16_to_f32((uint16_t)(w & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(w >> 16));
+  return (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
+}
+
 // 256 threads. s_cs: 64 doubles of LDS (cos, sin of the 32 angles). If q_abs is not null the
 // rotated query is also written into the RoPE part of the absorbed-query rows (operand order).
 __device__ __forceinline__ void rope_token_group(const CacheView& cache, int n_heads, int i, int g,
@@ -48,10 +62,8 @@ __device__ __forceinline__ void rope_token_group(const CacheView& cache, int n_h
   const int pos = token_pos[i];
 
   if (tid < kDr / 2) {
-    // theta_j = base^(-2j/d): exp2 of an exactly representable multiple of log2(base)
-    const double inv = exp2(-(2.0 * tid / kDr) * log2_theta);
     double s, c;
-    sincos((double)pos * inv, &s, &c);
+    rope_cos_sin(pos, tid, log2_theta, &c, &s);
     s_cs[tid] = c;
     s_cs[kDr / 2 + tid] = s;
   }
@@ -61,22 +73,12 @@ __device__ __forceinline__ void rope_token_group(const CacheView& cache, int n_h
     uint16_t* row = cache.data + row_offset(cache, token_seq[i], pos);
     // c_KV: 512 bf16 = 64 x 16 bytes, copied unchanged; k_R pair j rotated by angle j
     if (tid < kDc / 8) reinterpret_cast<uint4*>(row)[tid] = ckv;
-    if (tid < kDr / 2) {
-      const double x0 = bf16_to_f32((uint16_t)(kr & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(kr >> 16));
-      const double c = s_cs[tid], s = s_cs[kDr / 2 + tid];
-      reinterpret_cast<uint32_t*>(row + kDc)[tid] =
-          (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
-    }
+    if (tid < kDr / 2) reinterpret_cast<uint32_t*>(row + kDc)[tid] = rope_turn_pair(kr, s_cs[tid], s_cs[kDr / 2 + tid]);
   }
   if (qok) {
     uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * pc + e;
-      const double x0 = bf16_to_f32((uint16_t)(w[e] & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(w[e] >> 16));
-      const double c = s_cs[j], s = s_cs[kDr / 2 + j];
-      w[e] = (uint32_t)f64_to_bf16(x0 * c - x1 * s) | ((uint32_t)f64_to_bf16(x0 * s + x1 * c) << 16);
-    }
+    for (int e = 0; e < 4; ++e) w[e] = rope_turn_pair(w[e], s_cs[4 * pc + e], s_cs[kDr / 2 + 4 * pc + e]);
     const uint4 r = make_uint4(w[0], w[1], w[2], w[3]);
     *qp = r;
     if (q_abs != nullptr) *reinterpret_cast<uint4*>(q_abs + q_perm_offset(i, tiles, h, kDc + 8 * pc)) = r;

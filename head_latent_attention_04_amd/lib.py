@@ -44,6 +44,9 @@ EXPORTS = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_rope_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp,
                                        _vp, _vp]),
+    "mla_kv_down_append_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32]),
+    "mla_kv_down_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _i32,
+                                          _vp, _vp, ctypes.c_float, _vp, _sz, _vp]),
     "mla_decode_plan": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _i32, ctypes.POINTER(_i32),
                                        ctypes.POINTER(_i32)]),
     "mla_decode_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
@@ -122,7 +125,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_cache(data: torch.Tensor, block_table: Optional[torch.Tensor], max_blocks_per_seq: int) -> MlaCache:
-    """data: [num_blocks, 64, 576] bf16 (or its int16 view); block_table: [batch, max_blocks] int32 or None."""
+    """data: [num_blocks, 64, 576] bf16 (or its int16 view); block_table: [batch, max_blocks] int32 or None.
+
+    The descriptor holds raw device pointers: the caller keeps both tensors alive while it is used."""
     if data.dim() != 3 or data.shape[1] != BLOCK or data.shape[2] != ROW:
         raise ValueError("cache data must be [num_blocks, 64, 576]")
     return MlaCache(_ptr(data, "cache", BF16), data.shape[0], _ptr(block_table, "block_table", I32),
@@ -137,6 +142,22 @@ def rope_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_ro
         _ptr(k_rope, "k_rope", BF16, T * dims.d_rope),
         _ptr(q_rope, "q_rope", BF16, T * dims.n_heads * dims.d_rope), _stream(stream))
     _check("mla_rope_append", st)
+
+
+def kv_down_append_workspace_size(dims: MlaDims, num_tokens: int, dim: int) -> int:
+    return int(load().mla_kv_down_append_workspace_size(ctypes.byref(dims), num_tokens, dim))
+
+
+def kv_down_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, x, w_dkv, gamma, eps: float, workspace,
+                   stream=None):
+    T = token_seq.numel()
+    dim = x.shape[1] if x.dim() == 2 else 0
+    st = load().mla_kv_down_append(
+        ctypes.byref(dims), ctypes.byref(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        _ptr(token_pos, "token_pos", I32, T), _ptr(x, "x", BF16, T * dim), dim,
+        _ptr(w_dkv, "w_dkv", BF16, (dims.d_c + dims.d_rope) * dim), _ptr(gamma, "gamma", BF16, dims.d_c), eps,
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mla_kv_down_append", st)
 
 
 def decode_plan(dims: MlaDims, batch: int, max_seq_len: int, num_cus: int) -> Tuple[int, int]:

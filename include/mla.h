@@ -98,6 +98,31 @@ int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_to
                     const uint16_t* k_rope, uint16_t* q_rope_inout, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mla_kv_down_append - the KV down-projection of new tokens, fused with mla_rope_append's rotation
+ * and append ("论文复现工坊 No.4", section 2: kv_combined = wkv_a(x), split into the latent part and
+ * the decoupled RoPE key, the latent part through kv_norm; section 4: that RMSNorm follows the W_DKV
+ * projection).
+ * For each new token i: kv = x[i] . W_DKV^T (fp32 accumulation, rounded to bf16);
+ *   c_KV = bf16(kv[0:d_c] / sqrt(mean(kv[0:d_c]^2) + eps) * gamma);  k_R = kv[d_c:d_c+d_rope];
+ *   then the row [c_KV | R_p k_R] goes to the slot of (token_seq[i], token_pos[i]) exactly as
+ *   mla_rope_append writes it (no query).
+ *   x      [num_tokens, dim] bf16;  dim a positive multiple of 64 (else MLA_ERR_UNSUPPORTED)
+ *   w_dkv  [d_c + d_rope, dim] bf16 (the nn.Linear row layout of wkv_a)
+ *   gamma  [d_c] bf16 (kv_norm's weight);  eps >= 0 (finite)
+ *   workspace >= mla_kv_down_append_workspace_size(dims, num_tokens, dim) bytes (fp32 partial sums
+ *   over splits of the input dimension), 256-byte aligned
+ *   x and w_dkv 16-byte aligned; num_tokens <= 2097120
+ * Errors: MLA_ERR_NULL for a missing pointer, MLA_ERR_BAD_ARG for a negative count, a bad eps, a
+ * small or misaligned buffer, MLA_ERR_UNSUPPORTED for dim % 64 != 0. The workspace size query
+ * returns 0 for arguments the call would reject.
+ * Two launches on `stream`; num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+size_t mla_kv_down_append_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim);
+int mla_kv_down_append(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens, const int32_t* token_seq,
+                       const int32_t* token_pos, const uint16_t* x, int32_t dim, const uint16_t* w_dkv,
+                       const uint16_t* gamma, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Split planning for decode (host only, no HIP call).
  * Chooses split_tokens (a multiple of block_size) and num_splits = ceil(max_seq_len / split_tokens)
  * so that batch * num_splits work-groups fill `num_cus` compute units. Returns MLA_OK or an error.

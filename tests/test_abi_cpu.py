@@ -113,3 +113,36 @@ def test_plan_and_workspace_sizes():
     assert lib.decode_workspace_size(d, 32) == 32 * 128 * 576 * 2
     assert lib.decode_workspace_size(D(n_heads=120), 3) == 0
     assert lib.chunked_prefill_workspace_size(d, 2048) >= 2048 * 128 * 576 * 2
+
+
+def kvd(dims, c, T=1, dim=4096, eps=1e-6, ptrs=(FAKE,) * 5, ws=FAKE, wsb=1 << 40):
+    return lib.load().mla_kv_down_append(ctypes.byref(dims), ctypes.byref(c), T, ptrs[0], ptrs[1], ptrs[2], dim,
+                                         ptrs[3], ptrs[4], eps, ws, wsb, None)
+
+
+def test_kv_down_validation_and_workspace():
+    d = D()
+    assert kvd(d, cache(), dim=100) == lib.MLA_ERR_UNSUPPORTED
+    assert kvd(d, cache(), dim=0) == lib.MLA_ERR_BAD_ARG
+    assert kvd(d, cache(), dim=-64) == lib.MLA_ERR_BAD_ARG
+    assert kvd(d, cache(), T=-1) == lib.MLA_ERR_BAD_ARG
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert kvd(d, cache(), eps=eps) == lib.MLA_ERR_BAD_ARG
+    assert kvd(d, cache(), ptrs=(FAKE, FAKE, None, FAKE, FAKE)) == lib.MLA_ERR_NULL
+    assert kvd(d, cache(), ptrs=(FAKE, FAKE, FAKE, FAKE, None)) == lib.MLA_ERR_NULL
+    assert kvd(d, cache(), ws=None) == lib.MLA_ERR_NULL
+    assert kvd(d, cache(data=None)) == lib.MLA_ERR_NULL
+    assert kvd(d, cache(), wsb=1000) == lib.MLA_ERR_BAD_ARG
+    assert kvd(d, cache(), ws=FAKE + 16) == lib.MLA_ERR_BAD_ARG  # workspace needs 256-byte alignment
+    assert kvd(d, cache(), ptrs=(FAKE, FAKE, FAKE + 2, FAKE, FAKE)) == lib.MLA_ERR_BAD_ARG  # x: 16 bytes
+    assert kvd(d, cache(), ptrs=(FAKE, FAKE, FAKE, FAKE + 8, FAKE)) == lib.MLA_ERR_BAD_ARG  # w_dkv: 16 bytes
+    assert kvd(d, cache(), T=0, ptrs=(None,) * 5, ws=None, wsb=0) == lib.MLA_OK  # empty: no-op
+    assert kvd(D(n_heads=120), cache()) == lib.MLA_ERR_UNSUPPORTED
+    # 32 tokens of width 4096: fp32 partials of 16 input splits
+    assert lib.kv_down_append_workspace_size(d, 32, 4096) == 16 * 32 * 576 * 4
+    # 2048 tokens (tiled GEMM, 16 x 3 tiles of 128 x 192): 5 splits fill 240 of the 256 CUs
+    assert lib.kv_down_append_workspace_size(d, 2048, 4096) == 5 * 2048 * 576 * 4
+    # 20000 tokens: 157 x 3 tiles, one split
+    assert lib.kv_down_append_workspace_size(d, 20000, 4096) == 20000 * 576 * 4
+    assert lib.kv_down_append_workspace_size(d, 32, 100) == 0
+    assert lib.kv_down_append_workspace_size(d, -1, 4096) == 0

@@ -212,3 +212,48 @@ def make_config(i: int, seed: Optional[int] = None) -> Case:
     if i == 4:
         return make_case(CONFIG_NAMES[4], s, 128, [8192 + 1024] * 2, q_lens=[1024] * 2)
     raise ValueError(f"no config {i}")
+
+
+@dataclasses.dataclass
+class KvDownInputs:
+    """Inputs of the KV down-projection ahead of the append (bf16 bit patterns)."""
+    x: np.ndarray       # [T, dim] hidden states, N(0, 1)
+    w_dkv: np.ndarray   # [d_c + d_R, dim] wkv_a weight (nn.Linear layout), N(0, 1/dim)
+    gamma: np.ndarray   # [d_c] kv_norm weight, 1 + N(0, 0.25^2)
+
+
+def make_kv_down_inputs(seed: int, num_tokens: int, dim: int) -> KvDownInputs:
+    """Draw order: x -> w_dkv -> gamma (numpy PCG64).
+
+    The weight std 1/sqrt(dim) gives the projection unit-variance outputs. kv_norm's weight is
+    drawn around 1 rather than left at its all-ones initial value, so that each of its 512
+    entries is visible in the result.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal_bf16(rng, (num_tokens, dim))
+    w = _normal_bf16(rng, (D_C + D_ROPE, dim), 1.0 / math.sqrt(dim))
+    gamma = bf16_bits(1.0 + 0.25 * rng.standard_normal(D_C))
+    return KvDownInputs(x=x, w_dkv=w, gamma=gamma)
+
+
+def kv_down_layout(seq_lens: Sequence[int], new_lens: Sequence[int], seed: int):
+    """Token placement for an append of new tokens: sequence b receives its last new_lens[b]
+    positions (of seq_lens[b]). Only the 64-token blocks that receive a new token are mapped, in a
+    shuffled order; every other logical block of every sequence points at one spare block.
+    Returns (token_seq, token_pos, block_table, num_blocks, max_blocks_per_seq)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq_lens = np.asarray(seq_lens, np.int64)
+    B = len(seq_lens)
+    max_blocks = int((seq_lens.max() + BLOCK - 1) // BLOCK)
+    token_seq, token_pos, need = [], [], []
+    for b in range(B):
+        pos = np.arange(seq_lens[b] - new_lens[b], seq_lens[b])
+        token_seq.append(np.full(len(pos), b, np.int32))
+        token_pos.append(pos.astype(np.int32))
+        need += [(b, int(k)) for k in np.unique(pos // BLOCK)]
+    num_blocks = len(need) + 1
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    table = np.full((B, max_blocks), perm[-1], np.int32)
+    for j, (b, k) in enumerate(need):
+        table[b, k] = perm[j]
+    return np.concatenate(token_seq), np.concatenate(token_pos), table, num_blocks, max_blocks
