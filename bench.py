@@ -301,6 +301,17 @@ def prefill_flops(case):
     return attn, proj
 
 
+def expanded_flops(case):
+    """Algorithmic FLOP of the expanded form: the up-projection of every cached token of every sequence
+    (2 x 256 x 512 per token and head), then per query at position p, (p + 1) keys x n_h x
+    (2 x 192 score + 2 x 128 value)."""
+    H = case.n_heads
+    pos = case.q_positions().astype(np.float64)
+    up = float(np.sum(case.seq_lens)) * H * 2 * 256 * 512
+    attn = float(np.sum(pos + 1.0)) * H * (2 * 192 + 2 * 128)
+    return up + attn
+
+
 def prefill_cpu_baseline(case, budget_s):
     """fp64 expanded-form oracle on query tokens of the same prefill (all heads), until the budget
     is spent; rate in algorithmic TFLOP/s."""
@@ -343,6 +354,7 @@ def prefill_main(args, torch, lib, props):
     dc.prepare_step_inputs()
     dc.append_new()
     dc.alloc_prefill()
+    dc.alloc_prefill_expanded()
     torch.cuda.synchronize()
 
     def rope(i):
@@ -361,6 +373,10 @@ def prefill_main(args, torch, lib, props):
     torch.cuda.synchronize()
     ms_step = time_loop(torch, step, steps)
     ms = {"rope_append": time_each(torch, rope, steps), "chunked_prefill": time_each(torch, prefill, steps)}
+    # the same prefill in the expanded form (up-projected keys and values, 192-wide keys)
+    for i in range(2):
+        dc.prefill_expanded()
+    ms["chunked_prefill_expanded"] = time_each(torch, lambda i: dc.prefill_expanded(), steps)
     attn, proj = prefill_flops(case)
     total_q = int(case.cu_q_lens[-1])
     result = {
@@ -385,6 +401,11 @@ def prefill_main(args, torch, lib, props):
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flop_per_launch": attn + proj},
+        "expanded_form": {"kernels": "upproj_kernel + expanded_attn_kernel (mla_chunked_prefill_expanded)",
+                          "ms": round(ms["chunked_prefill_expanded"], 4),
+                          "speedup_vs_absorbed": round(ms["chunked_prefill"] / ms["chunked_prefill_expanded"], 3),
+                          "algorithmic_flop_per_launch": expanded_flops(case),
+                          "TFLOPs": round(expanded_flops(case) / (ms["chunked_prefill_expanded"] * 1e-3) / 1e12, 1)},
         "device": props.name,
     }
     if not args.no_cpu:

@@ -6,7 +6,7 @@
 // holds (BM/64) x (BN/64) accumulators of v_mfma_f32_32x32x16_bf16 (a 32 x 32 fp32 block each).
 // Operands stream global -> LDS with buffer_load ... lds in K stages of 64 (128 bytes per row), four
 // stage buffers deep (the whole 160 KB of LDS). A wave instruction moves eight whole 128-byte row segments: lane l fetches row
-// 8i + l/8 at 16-byte chunk (l % 8) ^ (row % 8) and lands at LDS offset 16 l, so a row's chunks sit
+// 8i + l/8 at 16-byte chunk (l % 8) ^ swz(row) and lands at LDS offset 16 l, so a row's chunks sit
 // XOR-swizzled by the row index and the MFMA operand reads (32 rows at one chunk) spread over the
 // banks. Rows of A past M are fetched from row M - 1 and never stored.
 #include <algorithm>
@@ -76,8 +76,11 @@ __device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
 }
 
-// LDS byte offset of (row, 16-byte chunk) inside one operand region of a stage
-__device__ __forceinline__ uint32_t seg_off(int row, int chunk) { return row * kRowSeg + 16 * (chunk ^ (row & 7)); }
+// LDS byte offset of (row, 16-byte chunk) of a stage: the chunk is XOR-swizzled by
+// swz(row) = (row ^ row / 8) % 8, which gives the rows that one LDS cycle serves (8 rows of one
+// 16-byte chunk for 32 banks, 16 rows for 64) distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ uint32_t seg_off(int row, int chunk) { return row * kRowSeg + 16 * (chunk ^ swz(row)); }
 
 }  // namespace
 
@@ -113,16 +116,19 @@ __global__ void __launch_bounds__(256) gemm_bt_partial_kernel(int M, int N, int 
   const i32x4 ra = buffer_rsrc(A, (uint32_t)((int64_t)M * K * 2));
   const i32x4 rb = buffer_rsrc(B, (uint32_t)((int64_t)N * K * 2));
   uint32_t va[kAInstr], vb[kBInstr];
-  const int rl = lane >> 3, chunk = (lane & 7) ^ rl;  // row base is a multiple of 8: row % 8 == rl
+  // lane l lands at LDS row lr (of the stage), slot l % 8, so it fetches chunk (l % 8) ^ swz(lr)
+  const int rl = lane >> 3;
 #pragma unroll
   for (int i = 0; i < kAInstr; ++i) {
-    const int r = min(m0 + (BM / 4) * wave + 8 * i + rl, M - 1);
-    va[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * chunk;
+    const int lr = (BM / 4) * wave + 8 * i + rl;
+    const int r = min(m0 + lr, M - 1);
+    va[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * ((lane & 7) ^ swz(lr));
   }
 #pragma unroll
   for (int i = 0; i < kBInstr; ++i) {
+    const int lr = BM + (BN / 4) * wave + 8 * i + rl;
     const int r = n0 + (BN / 4) * wave + 8 * i + rl;
-    vb[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * chunk;
+    vb[i] = (uint32_t)r * (uint32_t)(K * 2) + 16 * ((lane & 7) ^ swz(lr));
   }
   auto issue = [&](int st) {
     const uint32_t buf = lds0 + (uint32_t)((st % kNumBuf) * kStageBytes);

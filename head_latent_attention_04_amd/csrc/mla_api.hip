@@ -84,6 +84,32 @@ int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_to
                                           q_rope_inout, dims->rope_theta, stream));
 }
 
+size_t mla_chunked_prefill_expanded_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims) != MLA_OK || batch < 0 || max_seq_len < 0) return 0;
+  return mla::prefill_expanded_kv_bytes(batch, dims->n_heads, max_seq_len);
+}
+
+int mla_chunked_prefill_expanded(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                                 const int32_t* cu_q_lens, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                                 const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
+                                 const uint16_t* w_uv, void* workspace, size_t workspace_bytes, uint16_t* out,
+                                 float* lse_out, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_seq_len < 0) return MLA_ERR_BAD_ARG;
+  if (batch == 0 || total_q == 0) return MLA_OK;
+  if (max_q_len < 1 || max_seq_len < max_q_len) return MLA_ERR_BAD_ARG;
+  if (!seq_lens || !cu_q_lens || !q_nope || !q_rope || !w_uk || !w_uv || !workspace || !out) return MLA_ERR_NULL;
+  if (workspace_bytes < mla::prefill_expanded_kv_bytes(batch, dims->n_heads, max_seq_len)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0 || ((uintptr_t)q_nope & 15) != 0 || ((uintptr_t)q_rope & 15) != 0 ||
+      ((uintptr_t)out & 7) != 0)
+    return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_prefill_expanded(view(cache), batch, dims->n_heads, seq_lens, cu_q_lens, max_q_len,
+                                               max_seq_len, q_nope, q_rope, w_uk, w_uv, dims->scale, workspace, out,
+                                               lse_out, stream));
+}
+
 size_t mla_kv_down_append_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim) {
   if (check_dims(dims) != MLA_OK || num_tokens < 0 || dim <= 0 || dim % 64 != 0) return 0;
   return mla::kv_down_workspace_bytes(num_tokens, dim);

@@ -104,6 +104,14 @@ int gemm_bt_splits(int M, int N, int K);
 hipError_t launch_gemm_bt_partial(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
                                   hipStream_t stream);
 
+// Expanded-form chunked prefill: up-projected keys and values ([batch, n_heads, lpad, 128] each,
+// lpad = max_seq_len rounded up to 128, in the workspace), then causal attention with 192-wide keys.
+size_t prefill_expanded_kv_bytes(int batch, int n_heads, int max_seq_len);
+hipError_t launch_prefill_expanded(const CacheView& cache, int batch, int n_heads, const int32_t* seq_lens,
+                                   const int32_t* cu_q_lens, int max_q_len, int max_seq_len, const uint16_t* q_nope,
+                                   const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv, float scale,
+                                   void* workspace, uint16_t* out, float* lse_out, hipStream_t stream);
+
 // KV down-projection of num_tokens tokens (x [T, dim] . W_DKV^T, W_DKV [576, dim]), RMSNorm of the latent
 // part (eps, weight gamma [512]), then the RoPE rotation of k_R and the append, as launch_rope_append.
 // workspace: kv_down_workspace_bytes(num_tokens, dim) bytes (fp32 split partials).

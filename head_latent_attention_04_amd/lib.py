@@ -44,6 +44,9 @@ EXPORTS = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_rope_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp,
                                        _vp, _vp]),
+    "mla_chunked_prefill_expanded_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32]),
+    "mla_chunked_prefill_expanded": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp,
+                                                    _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "mla_kv_down_append_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32]),
     "mla_kv_down_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _i32,
                                           _vp, _vp, ctypes.c_float, _vp, _sz, _vp]),
@@ -142,6 +145,25 @@ def rope_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_ro
         _ptr(k_rope, "k_rope", BF16, T * dims.d_rope),
         _ptr(q_rope, "q_rope", BF16, T * dims.n_heads * dims.d_rope), _stream(stream))
     _check("mla_rope_append", st)
+
+
+def chunked_prefill_expanded_workspace_size(dims: MlaDims, batch: int, max_seq_len: int) -> int:
+    return int(load().mla_chunked_prefill_expanded_workspace_size(ctypes.byref(dims), batch, max_seq_len))
+
+
+def chunked_prefill_expanded(dims: MlaDims, cache: MlaCache, seq_lens, cu_q_lens, max_q_len: int, max_seq_len: int,
+                             q_nope, q_rope, w_uk, w_uv, workspace, out, lse_out=None, stream=None):
+    B = seq_lens.numel()
+    H = dims.n_heads
+    Tq = q_nope.shape[0]
+    st = load().mla_chunked_prefill_expanded(
+        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(cu_q_lens, "cu_q_lens", I32, B + 1), Tq, max_q_len, max_seq_len,
+        _ptr(q_nope, "q_nope", BF16, Tq * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, Tq * H * dims.d_rope),
+        _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out", BF16, Tq * H * dims.d_v), _ptr(lse_out, "lse_out", F32, Tq * H), _stream(stream))
+    _check("mla_chunked_prefill_expanded", st)
 
 
 def kv_down_append_workspace_size(dims: MlaDims, num_tokens: int, dim: int) -> int:

@@ -136,6 +136,20 @@ class DeviceCase:
                             self.q_nope, self.q_rope, self.w_uk, self.w_uv, self._pws, self.out, self.lse, stream)
 
 
+    def alloc_prefill_expanded(self):
+        Tq, H = self.case.total_q, self.case.n_heads
+        self.max_seq_len = int(self.case.seq_lens.max())
+        ws = lib.chunked_prefill_expanded_workspace_size(self.dims, self.case.batch, self.max_seq_len)
+        self._xws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
+        self.out_x = torch.empty((Tq, H, lib.D_V), dtype=torch.int16, device=self.device)
+        self.lse_x = torch.empty((Tq, H), dtype=torch.float32, device=self.device)
+
+    def prefill_expanded(self, stream=None):
+        lib.chunked_prefill_expanded(self.dims, self.cache, self.seq_lens, self.cu_q_lens, int(self.case.q_lens.max()),
+                                     self.max_seq_len, self.q_nope, self.q_rope, self.w_uk, self.w_uv, self._xws,
+                                     self.out_x, self.lse_x, stream)
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """bf16 bit patterns in an int16 device tensor -> float64 numpy."""
     a = t.detach().cpu().numpy().view(np.uint16).astype(np.uint32) << 16

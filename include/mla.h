@@ -243,6 +243,30 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
                         const uint16_t* w_uk, const uint16_t* w_uv, void* workspace,
                         size_t workspace_bytes, uint16_t* out, float* lse_out, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * mla_chunked_prefill_expanded - the same causal chunked prefill as mla_chunked_prefill, computed in
+ * the expanded form ("Multi-Head Latent Attention: DeepSeek V2/V3 工程视角" names the up-projection
+ * of the latent cache and its absorbed equivalent as the two ways to attend; "论文复现工坊 No.4",
+ * section 2: k_nope and v are the per-head split of wkv_b applied to c_KV, the score is
+ * q_nope . k_nope + q_R . k_R, scaled by 1/sqrt(d_nope + d_rope)):
+ *   k_nope[t, h] = W_UK[h] c_t,  v[t, h] = W_UV[h] c_t   (every cached token, rounded to bf16)
+ *   out[j, h, :] = sum_{t<=p} softmax_t(scale (q_nope[j,h] . k_nope[t,h] + q_rope[j,h] . kR_t)) v[t, h]
+ * Arguments as mla_chunked_prefill, plus
+ *   max_seq_len  host bound on every seq_lens[b] (sizes the up-projected keys and values), >= max_q_len
+ *   workspace >= mla_chunked_prefill_expanded_workspace_size(dims, batch, max_seq_len) bytes, 256-byte
+ *   aligned (2 x batch x n_heads x roundup(max_seq_len, 128) x 128 bf16); q_nope, q_rope 16-byte
+ *   aligned, out 8-byte aligned.
+ * Fewer multiply-adds than the absorbed form when a chunk attends to a long prefix; more memory
+ * traffic (the up-projected keys and values are written and read back). Two launches on `stream`.
+ * ------------------------------------------------------------------------------------------- */
+size_t mla_chunked_prefill_expanded_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_seq_len);
+int mla_chunked_prefill_expanded(const mla_dims* dims, const mla_cache* cache, int32_t batch,
+                                 const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t total_q,
+                                 int32_t max_q_len, int32_t max_seq_len, const uint16_t* q_nope,
+                                 const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv,
+                                 void* workspace, size_t workspace_bytes, uint16_t* out, float* lse_out,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,112 @@
+"""Parity of the expanded-form chunked prefill (mla_chunked_prefill_expanded) with the fp64 oracle, on
+the GPU. The oracle's prefill is itself the expanded form in fp64; the kernels round the up-projected
+keys and values to bf16 (one more rounding than the absorbed path, relative 2^-9 per element, which
+averages out over the softmax-weighted sum), so the same gates apply: relative Frobenius <= 5e-3 and
+max abs <= 2e-2 on the outputs, 1e-2 on the log-sum-exp (natural log)."""
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_04_amd.runner import DeviceCase, to_f64
+from oracle import mla_oracle as O
+from workloads import BF16_NAN, make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 5e-3
+MAX_ABS = 2e-2
+LSE_ABS = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def assert_close(got, ref, what, abs_scale=1.0):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = got - ref
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
+    mx = np.max(np.abs(err)) if err.size else 0.0
+    say(f"  {what}: rel_fro={rel:.3e} max_abs={mx:.3e} (gate {MAX_ABS * abs_scale:.3e})")
+    assert rel <= REL_FRO and mx <= MAX_ABS * abs_scale
+
+
+def oracle_inputs(case):
+    cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
+    cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
+                             case.c_kv, case.k_rope)
+    q_rot = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(case.q_rope), case.q_positions()[:, None]))
+    return cache, q_rot
+
+
+def run_expanded(case):
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.append_new()
+    dc.alloc_prefill_expanded()
+    dc.prefill_expanded()
+    torch.cuda.synchronize()
+    return dc, to_f64(dc.out_x), dc.lse_x.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("H,lens,qlens", [
+    (16, [70, 33], [40, 33]),            # the first key tile partly masked, a sequence that is all chunk
+    (32, [200, 1], [65, 1]),             # a one-token sequence
+    (128, [130], [130]),                 # one query tile, 130 queries: the second wave partly live
+    (160, [90, 40], [20, 40]),           # five head groups of 32
+    (16, [700, 300], [600, 300]),        # three and two query tiles of 256, two up-projection tiles each
+    (16, [100, 50, 80], [30, 0, 80]),    # an empty chunk in the middle
+])
+def test_prefill_expanded_matches_oracle(H, lens, qlens):
+    say(f"[prefill expanded] H={H} lens={lens} q={qlens}")
+    case = make_case("prefill_x", 62, H, lens, q_lens=qlens, paged=True, spare_blocks=2)
+    dc, out, lse = run_expanded(case)
+    cache, q_rot = oracle_inputs(case)
+    ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.cu_q_lens,
+                        case.q_nope, q_rot, case.w_uk, case.w_uv)
+    assert_close(out, ref, "prefill expanded")
+    assert np.max(np.abs(lse - rl)) <= LSE_ABS
+
+
+def test_prefill_expanded_rescales_on_score_growth():
+    """RoPE keys of positions >= 100 scaled by 2^5 (exact in bf16): later key tiles' scores exceed the
+    first tile's max by far more than the 2^8 the weights may grow between rescales, so the running
+    max moves and the accumulators are rescaled; the result still matches the oracle.
+
+    The softmax is then nearly one-hot, so an output is close to one up-projected value row (|v| up
+    to about 4, where the bf16 rounding of v alone moves it by up to 2^-9 |v| and the output's own
+    rounding by as much again): the max-abs gate is taken relative to max(1, max |ref|)."""
+    say("[prefill expanded] score growth")
+    case = make_case("growth_x", 72, 16, [400], q_lens=[300], paged=True, spare_blocks=2)
+    big = case.token_pos >= 100
+    kr = case.k_rope.astype(np.uint32)
+    nonzero = ((kr >> 7) & 0xFF) > 0
+    case.k_rope = (kr + (np.uint32(5) << 7) * (big[:, None] & nonzero)).astype(np.uint16)
+    cache, q_rot = oracle_inputs(case)
+    rows = O.gather_rows(cache, case.block_table, case.max_blocks_per_seq, 0, 400)
+    s = (O.bf16_to_f64(q_rot[0]) @ rows[:, 512:].T) / np.sqrt(192) * np.log2(np.e)
+    assert np.max(s[:, 128:].max(axis=1) - s[:, :64].max(axis=1)) > 8
+    dc, out, lse = run_expanded(case)
+    ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.cu_q_lens,
+                        case.q_nope, q_rot, case.w_uk, case.w_uv)
+    assert_close(out, ref, "growth", abs_scale=max(1.0, float(np.max(np.abs(ref)))))
+    assert np.max(np.abs(lse - rl)) <= LSE_ABS
+
+
+def test_prefill_expanded_config4_full_size_sampled():
+    """2 sequences, 1024 new tokens after 8192 cached, 128 heads: every output finite; sampled (query,
+    head) outputs, the first and last query of each sequence among them, match the oracle."""
+    say("[prefill expanded] config 4 full size")
+    case = make_config(4)
+    dc, out, lse = run_expanded(case)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(40)
+    cu = case.cu_q_lens
+    rows = sorted(set([int(cu[0]), int(cu[1]) - 1, int(cu[1]), int(cu[2]) - 1] + rng.integers(0, int(cu[-1]), 2).tolist()))
+    heads = sorted(set([0, case.n_heads - 1] + rng.integers(0, case.n_heads, 4).tolist()))
+    cache, q_rot = oracle_inputs(case)
+    ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, cu, case.q_nope, q_rot,
+                        case.w_uk, case.w_uv, rows_sel=rows, heads=heads)
+    sel = np.ix_(rows, heads)
+    assert_close(out[sel], ref[sel], "config 4 sampled")
+    assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
