@@ -10,9 +10,10 @@
 //
 // Two kernels:
 //   1. upproj_kernel: [K_up | V_up](b, h, t) = [W_UK[h]; W_UV[h]] c_t for every cached token t of every
-//      sequence (bf16 out, fp32 accumulation). Work-group (128 tokens, head); the A operand is the
-//      head's 256 weight rows, the B operand the tokens' latents, both through LDS in K stages of 64.
-//   2. expanded_attn_kernel: work-group (256 queries of one sequence, head), wave w owns 64 queries.
+//      sequence (bf16 out, fp32 accumulation). Work-group (256 tokens, head), 8 waves; the A operand
+//      is the head's 256 weight rows, the B operand the tokens' latents, both through LDS in K stages
+//      of 64.
+//   2. expanded_attn_kernel: work-group (256 queries of one sequence, head), 8 waves of 32 queries.
 //      Keys stream in 64-key stages (K_up, k_R from the cache rows, V_up) through LDS. Scores are
 //      S^T = K Q^T (queries in registers as the B operand), so every lane holds one query's scores
 //      and the softmax weights become the B operand of O^T += V^T P^T without leaving registers;
@@ -98,8 +99,17 @@ __device__ __forceinline__ int xcd_logical(int h, int G) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
 }
 
+// Base of (seq, logical block) in the cache; seq and blk are wave-uniform. The table is read through
+// the constant address space, i.e. with a scalar load (counted by lgkmcnt): a vector load would make
+// its wait also drain the stage copies in flight.
 __device__ __forceinline__ const uint16_t* block_base(const CacheView& c, int seq, int blk) {
-  const int64_t phys = c.table ? (int64_t)c.table[(int64_t)seq * c.max_blocks + blk] : (int64_t)seq * c.max_blocks + blk;
+  const __attribute__((address_space(4))) int32_t* tab = (const __attribute__((address_space(4))) int32_t*)c.table;
+  int64_t phys;
+  if (c.table) {
+    phys = (int64_t)__builtin_amdgcn_readfirstlane(tab[(int64_t)seq * c.max_blocks + blk]);
+  } else {
+    phys = (int64_t)seq * c.max_blocks + blk;
+  }
   return c.data + phys * (int64_t)(kBlock * kRow);
 }
 
@@ -110,16 +120,18 @@ __device__ __forceinline__ uint32_t pack_bf16x4_lo(float a, float b) {
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------
-// Up-projection. Work-group (head h, token tile mt of sequence b): D[n][t] = sum_k W[n][k] c_t[k],
-// n < 256 the head's W_UK rows then W_UV rows, t the tile's 128 tokens, k over the 512 latents.
-// Stage (64 of k) in LDS: rows 0..127 the tokens' latents, rows 128..383 the weight rows.
-// Waves 2 x 2: wave (wn, wm) computes weight rows 128 wn .. +127 (wn = 0: keys, 1: values) for
-// tokens 64 wm .. +63 as 4 x 2 blocks of 32 x 32.
-constexpr int kUpTok = 128, kUpW = 256, kUpStages = 3;
-constexpr int kUpStageBytes = (kUpTok + kUpW) * kSeg;  // 48 KB
-constexpr int kUpInstr = 12;                             // copy instructions per wave per stage
+// Up-projection. Work-group (head h, 256-token tile mt of sequence b), eight waves:
+// D[n][t] = sum_k W[n][k] c_t[k], n < 256 the head's W_UK rows then W_UV rows, t the tile's tokens,
+// k over the 512 latents in stages of 64. Stage in LDS: rows 0..255 the tokens' latents, rows
+// 256..511 the weight rows (64 KB; two stage buffers). Wave (wn, wm) = (w / 4, w % 4) computes weight
+// rows 128 wn .. +127 (wn = 0: keys, 1: values) for tokens 64 wm .. +63 as 4 x 2 blocks of 32 x 32.
+// The larger tile (against 128 tokens) cuts the bytes copied into LDS per multiply-add by a third.
+constexpr int kUpTok = 256, kUpW = 256, kUpWaves = 8, kUpStages = 2;
+constexpr int kUpStageBytes = (kUpTok + kUpW) * kSeg;  // 64 KB
+constexpr int kUpInstr = 8;                              // copy instructions per wave per stage
+constexpr int kUpPad = 128;                              // lpad granule
 
-__global__ void __launch_bounds__(256) upproj_kernel(CacheView cache, const int32_t* __restrict__ seq_lens,
+__global__ void __launch_bounds__(512) upproj_kernel(CacheView cache, const int32_t* __restrict__ seq_lens,
                                                      int n_heads, int mtiles, int lpad,
                                                      const uint16_t* __restrict__ w_uk,
                                                      const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ k_up,
@@ -139,9 +151,9 @@ __global__ void __launch_bounds__(256) upproj_kernel(CacheView cache, const int3
   const int last = len - 1;
   const int blk = min((m0 + 32 * wave) / kBlock, last / kBlock);
   const i32x4 rc = buffer_rsrc(block_base(cache, b, blk), kBlock * kRowBytes);
-  // weights: wave w copies rows 64 (w % 2) .. +63 of W_UK[h] (w < 2) or W_UV[h]
-  const i32x4 rw = buffer_rsrc((wave < 2 ? w_uk : w_uv) + (int64_t)h * kDnope * kDc, kDnope * kDc * 2);
-  uint32_t voff[kUpInstr], mofs[kUpInstr];
+  // weights: wave w copies rows 32 (w % 4) .. +31 of W_UK[h] (w < 4) or W_UV[h] (w >= 4)
+  const i32x4 rw = buffer_rsrc((wave < 4 ? w_uk : w_uv) + (int64_t)h * kDnope * kDc, kDnope * kDc * 2);
+  uint32_t voff[kUpInstr];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = 32 * wave + 8 * i + rl;
@@ -149,25 +161,25 @@ __global__ void __launch_bounds__(256) upproj_kernel(CacheView cache, const int3
     if (tok > last) tok = last;
     const int row = (tok / kBlock == blk) ? tok % kBlock : last % kBlock;
     voff[i] = (uint32_t)(row * kRowBytes + 16 * ((lane & 7) ^ swz(lr)));
-    mofs[i] = (uint32_t)((32 * wave + 8 * i) * kSeg);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int lr = kUpTok + 64 * wave + 8 * i + rl;
-    const int row = 64 * (wave & 1) + 8 * i + rl;
+  for (int i = 0; i < 4; ++i) {
+    const int lr = kUpTok + 32 * wave + 8 * i + rl;
+    const int row = 32 * (wave & 3) + 8 * i + rl;
     voff[4 + i] = (uint32_t)(row * kDc * 2 + 16 * ((lane & 7) ^ swz(lr)));
-    mofs[4 + i] = (uint32_t)((kUpTok + 64 * wave + 8 * i) * kSeg);
   }
   auto issue = [&](int st) {
     const uint32_t buf = lds0 + (uint32_t)((st % kUpStages) * kUpStageBytes);
     const uint32_t soff = (uint32_t)(st * kSeg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) copy_seg(rc, voff[i], soff, __builtin_amdgcn_readfirstlane(buf + mofs[i]));
+    for (int i = 0; i < 4; ++i)
+      copy_seg(rc, voff[i], soff, __builtin_amdgcn_readfirstlane(buf + (32 * wave + 8 * i) * kSeg));
 #pragma unroll
-    for (int i = 4; i < kUpInstr; ++i) copy_seg(rw, voff[i], soff, __builtin_amdgcn_readfirstlane(buf + mofs[i]));
+    for (int i = 0; i < 4; ++i)
+      copy_seg(rw, voff[4 + i], soff, __builtin_amdgcn_readfirstlane(buf + (kUpTok + 32 * wave + 8 * i) * kSeg));
   };
 
-  const int wn = wave >> 1, wm = wave & 1, khalf = lane >> 5;
+  const int wn = wave >> 2, wm = wave & 3, khalf = lane >> 5;
   const int wrow0 = kUpTok + 128 * wn + (lane & 31), trow0 = 64 * wm + (lane & 31);
   f32x16 acc[4][2];
 #pragma unroll
@@ -177,14 +189,10 @@ __global__ void __launch_bounds__(256) upproj_kernel(CacheView cache, const int3
 
   constexpr int nst = kDc / 64;  // 8 stages
   issue(0);
-  issue(1);
   for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst)
-      wait_vmcnt<kUpInstr>();
-    else
-      wait_vmcnt<0>();
-    wg_barrier();  // stage st is in LDS; every wave is done with stage st - 1, whose buffer st + 2 reuses
-    if (st + 2 < nst) issue(st + 2);
+    wait_vmcnt<0>();
+    wg_barrier();  // stage st is in LDS; every wave is done with stage st - 1, whose buffer st + 1 reuses
+    if (st + 1 < nst) issue(st + 1);
     const lds_char* buf = lds + (st % kUpStages) * kUpStageBytes;
     bf16x8 wa[2][4], tb[2][2];
     auto load = [&](int kk, int slot) {
@@ -206,11 +214,13 @@ __global__ void __launch_bounds__(256) upproj_kernel(CacheView cache, const int3
   }
 
   // D layout: lane holds token column lane % 32 and weight rows 8 (e / 4) + 4 (lane / 32) + e % 4 of
-  // a block: four consecutive output elements per (block, e / 4), stored as 8 bytes
+  // a block: four consecutive output elements per (block, e / 4), stored as 8 bytes. Rows past lpad
+  // (a last tile that overhangs it) are not stored.
   uint16_t* dst = (wn == 0 ? k_up : v_up) + ((int64_t)(b * n_heads + h) * lpad) * kDnope;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = m0 + 64 * wm + 32 * i + (lane & 31);
+    if (t >= lpad) continue;
     uint16_t* drow = dst + (int64_t)t * kDnope;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -225,15 +235,18 @@ __global__ void __launch_bounds__(256) upproj_kernel(CacheView cache, const int3
 }
 
 // ------------------------------------------------------------------------------------------------
-// Attention. Stage = 64 keys in five LDS sub-tiles of 64 rows x 128 bytes: 0, 1 = K_up columns 0-63,
-// 64-127; 2 = k_R (from the cache rows); 3, 4 = V_up columns 0-63, 64-127.
-constexpr int kFaQ = 256, kFaKeys = 64, kFaStages = 3;
+// Attention. Work-group (256 queries of one sequence, head): eight waves, two per SIMD, wave w owns
+// queries 32 w .. +31, so one wave's softmax (VALU) runs beside the other wave's MFMAs. Stage = 64
+// keys in five LDS sub-tiles of 64 rows x 128 bytes: 0, 1 = K_up columns 0-63, 64-127; 2 = k_R (from
+// the cache rows); 3, 4 = V_up columns 0-63, 64-127. Copy instruction i of wave w moves rows
+// 8 w .. +7 of sub-tile i.
+constexpr int kFaQ = 256, kFaWaves = 8, kFaKeys = 64, kFaStages = 3;
 constexpr int kFaSub = kFaKeys * kSeg;        // 8 KB
 constexpr int kFaStageBytes = 5 * kFaSub;     // 40 KB
-constexpr int kFaInstr = 10;                  // copy instructions per wave per stage
+constexpr int kFaInstr = 5;                   // copy instructions per wave per stage
 constexpr float kRescaleExcess = 8.0f;        // log2 units: weights stay below 2^8 between rescales
 
-__global__ void __launch_bounds__(256) expanded_attn_kernel(CacheView cache, const int32_t* __restrict__ seq_lens,
+__global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, const int32_t* __restrict__ seq_lens,
                                                             const int32_t* __restrict__ cu_q_lens, int n_heads,
                                                             int qtiles, int lpad, const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ q_rope,
@@ -251,68 +264,62 @@ __global__ void __launch_bounds__(256) expanded_attn_kernel(CacheView cache, con
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, khalf = lane >> 5;
   const int wg_last = min(qt * kFaQ + kFaQ - 1, qlen - 1);
   const int nkt = (pos0 + wg_last + 1 + kFaKeys - 1) / kFaKeys;  // key tiles the work-group needs
-  const int w_first = qt * kFaQ + 64 * wave;                    // the wave's first query (chunk index)
+  const int w_first = qt * kFaQ + 32 * wave;                    // the wave's first query (chunk index)
   const bool w_live = w_first < qlen;
-  const int w_last = min(w_first + 63, qlen - 1);
+  const int w_last = min(w_first + 31, qlen - 1);
   const int w_nkt = w_live ? (pos0 + w_last + 1 + kFaKeys - 1) / kFaKeys : 0;
 
-  // queries of the lane: chunk index jq[qb] (clamped into the chunk), position pq[qb]
-  int jq[2], pq[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    jq[qb] = min(w_first + 32 * qb + (lane & 31), qlen - 1);
-    pq[qb] = pos0 + jq[qb];
-  }
-  // Q^T operand (B): query jq[qb], elements 16 ks + 8 khalf .. +7 of [q_nope | q_R]
-  bf16x8 qop[2][12];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t row = (int64_t)(q0 + jq[qb]) * n_heads + h;
+  // the lane's query: chunk index jq (clamped into the chunk), position pq
+  const int jq = min(w_first + (lane & 31), qlen - 1);
+  const int pq = pos0 + jq;
+  // Q^T operand (B): query jq, elements 16 ks + 8 khalf .. +7 of [q_nope | q_R]
+  bf16x8 qop[12];
+  {
+    const int64_t row = (int64_t)(q0 + jq) * n_heads + h;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) {
       const int d = 16 * ks + 8 * khalf;
-      qop[qb][ks] = ks < 8 ? *reinterpret_cast<const bf16x8*>(q_nope + row * kDnope + d)
-                           : *reinterpret_cast<const bf16x8*>(q_rope + row * kDr + (d - kDnope));
+      qop[ks] = ks < 8 ? *reinterpret_cast<const bf16x8*>(q_nope + row * kDnope + d)
+                       : *reinterpret_cast<const bf16x8*>(q_rope + row * kDr + (d - kDnope));
     }
   }
+  // The query loads complete here, with a wait the compiler sees: otherwise it guards the loop's
+  // MFMAs with waits on its own count of outstanding loads, which the stage copies would also satisfy
+  // only once they complete.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0, expcnt 7, lgkmcnt 15 (gfx9 encoding)
 
-  // copy descriptors: instruction i of wave w is global instruction g = 4 i + w: sub-tile g / 8, rows
-  // 8 (g % 8) .. +7. Lane l fetches row r = 8 (g % 8) + l / 8 at chunk (l % 8) ^ swz(r).
   const int64_t kv_base = ((int64_t)(b * n_heads + h) * lpad) * kDnope;
-  const int rl = lane >> 3;
   auto issue = [&](int kt) {
-    const uint32_t buf = lds0 + (uint32_t)((kt % kFaStages) * kFaStageBytes);
+    const uint32_t buf = lds0 + (uint32_t)((kt % kFaStages) * kFaStageBytes) + (uint32_t)(8 * wave * kSeg);
     const int t0 = kt * kFaKeys;
     const i32x4 rk = buffer_rsrc(k_up + kv_base + (int64_t)t0 * kDnope, kFaKeys * kDnope * 2);
     const i32x4 rv = buffer_rsrc(v_up + kv_base + (int64_t)t0 * kDnope, kFaKeys * kDnope * 2);
     const i32x4 rr = buffer_rsrc(block_base(cache, b, kt), kBlock * kRowBytes);
-#pragma unroll
-    for (int i = 0; i < kFaInstr; ++i) {
-      const int g = 4 * i + wave;
-      const int sub = g >> 3, r = 8 * (g & 7) + rl;
-      const int chunk = (lane & 7) ^ swz(r);
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(buf + sub * kFaSub + 8 * (g & 7) * kSeg);
-      if (sub == 2) {
-        copy_seg(rr, (uint32_t)(r * kRowBytes + kDc * 2 + 16 * chunk), 0, m0);
-      } else {
-        const int half = (sub < 2 ? sub : sub - 3);
-        copy_seg(sub < 2 ? rk : rv, (uint32_t)(r * kDnope * 2 + half * kSeg + 16 * chunk), 0, m0);
-      }
-    }
+    // lane l lands at row r = 8 w + l / 8, slot l % 8 of each sub-tile, so it fetches chunk
+    // (l % 8) ^ swz(r); the offsets are recomputed here rather than held across the loop (the empty
+    // asm makes the lane index opaque at this point)
+    int lv = lane;
+    asm volatile("" : "+v"(lv));
+    const int r = 8 * wave + (lv >> 3);
+    const int c16 = 16 * ((lv & 7) ^ swz(r));
+    const uint32_t okv = (uint32_t)(r * kDnope * 2 + c16);
+    copy_seg(rk, okv, 0, __builtin_amdgcn_readfirstlane(buf + 0 * kFaSub));
+    copy_seg(rk, okv + kSeg, 0, __builtin_amdgcn_readfirstlane(buf + 1 * kFaSub));
+    copy_seg(rr, (uint32_t)(r * kRowBytes + kDc * 2 + c16), 0, __builtin_amdgcn_readfirstlane(buf + 2 * kFaSub));
+    copy_seg(rv, okv, 0, __builtin_amdgcn_readfirstlane(buf + 3 * kFaSub));
+    copy_seg(rv, okv + kSeg, 0, __builtin_amdgcn_readfirstlane(buf + 4 * kFaSub));
   };
 
   // K operand (A): key row 32 kb + lane % 32, elements 16 ks + 8 khalf: sub-tile ks / 4 (ks < 8) or
-  // 2 (k_R), chunk 2 (ks % 4) + khalf
+  // 2 (k_R), chunk 2 (ks % 4) + khalf.
   // V^T operand (A, transposing reads): in 16-lane group g, lane r reads key row
-  //   32 kb + 16 half + 8 rd + 4 (g / 2) + r / 4 at value column 32 dblk + 16 (g % 2) + 4 (r % 4)
-  // and receives column 32 dblk + lane % 32 of 4 keys: the key order of the weights' B operand.
+  //   32 kb + 16 half + 8 rd + 4 (g / 2) + r / 4 at value column 32 j + 16 (g % 2) + 4 (r % 4)
+  // and receives column 32 j + lane % 32 of 4 keys: the key order of the weights' B operand.
   const int g16 = lane >> 4, r16 = lane & 15;
-  float m_ref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  f32x16 o[4][2];
+  float m_ref = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[j][qb] = f32x16{};
+  for (int j = 0; j < 4; ++j) o[j] = f32x16{};
 
   issue(0);
   if (nkt > 1) issue(1);
@@ -326,66 +333,50 @@ __global__ void __launch_bounds__(256) expanded_attn_kernel(CacheView cache, con
     if (kt >= w_nkt) continue;  // every key of this tile is after the wave's last query
     const lds_char* buf = lds + (kt % kFaStages) * kFaStageBytes;
     const int t0 = kt * kFaKeys;
-
     const bool masked = t0 + kFaKeys - 1 > pos0 + w_first;
-    // The tile is taken as two halves of 32 keys: scores, softmax and the value product of one half
-    // before the next, which halves the registers the scores and weights occupy.
+    // two halves of 32 keys: scores, softmax, value product
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // scores S^T[key][query] for the half's 32 keys x the wave's 2 x 32 queries
-      f32x16 sc[2] = {f32x16{}, f32x16{}};
+      f32x16 sc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) {
         const int sub = ks < 8 ? ks >> 2 : 2;
         const bf16x8 kop = lds_b128(buf + sub * kFaSub + seg_off(32 * kb + (lane & 31), 2 * (ks & 3) + khalf));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][ks], sc[qb], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sc, 0, 0, 0);
       }
-
-      // softmax: lane holds query jq[qb] and keys t0 + 32 kb + 8 (e / 4) + 4 khalf + e % 4
-      float mx[2] = {-INFINITY, -INFINITY};
+      // softmax: lane holds query jq and keys t0 + 32 kb + 8 (e / 4) + 4 khalf + e % 4; the max is
+      // taken on the raw scores (scale > 0), masked keys become -inf
+      float mx = -INFINITY;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = sc[qb][e] * scale_log2;
-          if (masked) {
-            const int t = t0 + 32 * kb + 8 * (e >> 2) + 4 * khalf + (e & 3);
-            if (t > pq[qb]) v = -INFINITY;
-          }
-          sc[qb][e] = v;
-          mx[qb] = fmaxf(mx[qb], v);
+      for (int e = 0; e < 16; ++e) {
+        if (masked) {
+          const int t = t0 + 32 * kb + 8 * (e >> 2) + 4 * khalf + (e & 3);
+          if (t > pq) sc[e] = -INFINITY;
         }
+        mx = fmaxf(mx, sc[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      if (__any(mx > m_ref + kRescaleExcess)) {
+        const float mn = fmaxf(m_ref, mx);
+        const float f = exp2f(m_ref - mn);  // 0 on the first tile (m_ref = -inf)
+        lsum *= f;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 32));
-      const bool need = mx[0] > m_ref[0] + kRescaleExcess || mx[1] > m_ref[1] + kRescaleExcess;
-      if (__any(need)) {
+        for (int j = 0; j < 4; ++j) o[j] *= f;
+        m_ref = mn;
+      }
+      // p = 2^(scale_log2 s - m_ref) <= 2^8 (v_exp_f32: arguments below -126 give 0, weights below
+      // fp32's normal range anyway)
+      const float nm = -m_ref;
+      bf16x8 pk[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float mn = fmaxf(m_ref[qb], mx[qb]);
-          const float f = exp2f(m_ref[qb] - mn);  // 0 on the first tile (m_ref = -inf)
-          lsum[qb] *= f;
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j][qb] *= f;
-          m_ref[qb] = mn;
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * half + e], scale_log2, nm));
+          lsum += p;
+          pk[half][e] = (__bf16)p;
         }
       }
-      bf16x8 pk[2][2];  // [qb][half]: the weights of keys 32 kb + 16 half .. +15
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = exp2f(sc[qb][8 * half + e] - m_ref[qb]);
-            lsum[qb] += p;
-            v[e] = (__bf16)p;
-          }
-          pk[qb][half] = v;
-        }
-
       // O^T[value column][query] += V^T P^T over the half's 32 keys
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -400,9 +391,7 @@ __global__ void __launch_bounds__(256) expanded_attn_kernel(CacheView cache, con
             t[rd] = lds_tr16(buf + sub * kFaSub + r * kSeg + 16 * (chunk ^ swz(r)) + 8 * (r16 & 1));
           }
           const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[j][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[qb][half], o[j][qb], 0, 0, 0);
+          o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[half], o[j], 0, 0, 0);
         }
       }
     }
@@ -410,29 +399,26 @@ __global__ void __launch_bounds__(256) expanded_attn_kernel(CacheView cache, con
   if (!w_live) return;
 
   // out[j, h, d] = O / l; lanes l and l ^ 32 hold the same query (different keys and value rows)
+  const float tot = lsum + __shfl_xor(lsum, 32);
+  const float inv = 1.f / tot;
+  const int jl = w_first + (lane & 31);
+  if (jl >= qlen) return;
+  const int64_t row = (int64_t)(q0 + jl) * n_heads + h;
+  uint16_t* orow = out + row * kDv;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float tot = lsum[qb] + __shfl_xor(lsum[qb], 32);
-    const float inv = 1.f / tot;
-    const int jl = w_first + 32 * qb + (lane & 31);
-    if (jl >= qlen) continue;
-    const int64_t row = (int64_t)(q0 + jl) * n_heads + h;
-    uint16_t* orow = out + row * kDv;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int d = 32 * j + 8 * e4 + 4 * khalf;
-        const uint2 v = make_uint2(pack_bf16x4_lo(o[j][qb][4 * e4] * inv, o[j][qb][4 * e4 + 1] * inv),
-                                   pack_bf16x4_lo(o[j][qb][4 * e4 + 2] * inv, o[j][qb][4 * e4 + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + d) = v;
-      }
-    if (lse_out != nullptr && khalf == 0) lse_out[row] = (m_ref[qb] + log2f(tot)) * 0.6931471805599453f;
-  }
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int d = 32 * j + 8 * e4 + 4 * khalf;
+      const uint2 v = make_uint2(pack_bf16x4_lo(o[j][4 * e4] * inv, o[j][4 * e4 + 1] * inv),
+                                 pack_bf16x4_lo(o[j][4 * e4 + 2] * inv, o[j][4 * e4 + 3] * inv));
+      *reinterpret_cast<uint2*>(orow + d) = v;
+    }
+  if (lse_out != nullptr && khalf == 0) lse_out[row] = (m_ref + log2f(tot)) * 0.6931471805599453f;
 }
 
 size_t prefill_expanded_kv_bytes(int batch, int n_heads, int max_seq_len) {
-  const size_t lpad = (size_t)((max_seq_len + kUpTok - 1) / kUpTok) * kUpTok;
+  const size_t lpad = (size_t)((max_seq_len + kUpPad - 1) / kUpPad) * kUpPad;
   return 2 * (size_t)batch * n_heads * lpad * kDnope * 2;
 }
 
@@ -441,19 +427,19 @@ hipError_t launch_prefill_expanded(const CacheView& cache, int batch, int n_head
                                    const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv, float scale,
                                    void* workspace, uint16_t* out, float* lse_out, hipStream_t stream) {
   const int mtiles = (max_seq_len + kUpTok - 1) / kUpTok;
-  const int lpad = mtiles * kUpTok;
+  const int lpad = (max_seq_len + kUpPad - 1) / kUpPad * kUpPad;
   uint16_t* k_up = static_cast<uint16_t*>(workspace);
   uint16_t* v_up = k_up + (size_t)batch * n_heads * lpad * kDnope;
   const int64_t g1 = (int64_t)batch * mtiles * n_heads;
   const int qtiles = (max_q_len + kFaQ - 1) / kFaQ;
   const int64_t g2 = (int64_t)batch * n_heads * qtiles;
   if (g1 > 0x7FFFFFFF || g2 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(upproj_kernel, dim3((unsigned)g1), dim3(256), 0, stream, cache, seq_lens, n_heads, mtiles, lpad, w_uk,
+  hipLaunchKernelGGL(upproj_kernel, dim3((unsigned)g1), dim3(kUpWaves * 64), 0, stream, cache, seq_lens, n_heads, mtiles, lpad, w_uk,
                      w_uv, k_up, v_up);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(expanded_attn_kernel, dim3((unsigned)g2), dim3(256), 0, stream, cache, seq_lens, cu_q_lens, n_heads,
+  hipLaunchKernelGGL(expanded_attn_kernel, dim3((unsigned)g2), dim3(kFaWaves * 64), 0, stream, cache, seq_lens, cu_q_lens, n_heads,
                      qtiles, lpad, q_nope, q_rope, k_up, v_up, scale_log2, out, lse_out);
   return hipGetLastError();
 }
