@@ -45,10 +45,11 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "prefill", "kv_down"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "prefill_crossover", "kv_down"], default="decode",
                     help="decode: B=32, n_h=128, 4K context (the headline); prefill: chunked prefill, 2 x 1024 "
-                         "new tokens after 8192 cached; kv_down: KV down-projection + kv_norm + RoPE append of "
-                         "the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096")
+                         "new tokens after 8192 cached; prefill_crossover: absorbed against expanded prefill over "
+                         "chunk lengths 64..2048 after 8192 cached; kv_down: KV down-projection + kv_norm + RoPE "
+                         "append of the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096")
     return ap.parse_args()
 
 
@@ -159,6 +160,8 @@ def main():
         return prefill_main(args, torch, lib, props)
     if args.workload == "kv_down":
         return kv_down_main(args, torch, lib, props)
+    if args.workload == "prefill_crossover":
+        return crossover_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -410,6 +413,46 @@ def prefill_main(args, torch, lib, props):
     }
     if not args.no_cpu:
         result["cpu_baseline"] = prefill_cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def crossover_main(args, torch, lib, props):
+    """Both prefill forms over chunk lengths q (2 sequences, 128 heads, 8192 tokens cached before the
+    chunk): the expanded form pays 2 x 256 x 512 per (cached token, head) for the up-projection and
+    saves 2 x (576 + 512 - 192 - 128) per (query, key, head), so it wins once the chunk is long enough."""
+    from head_latent_attention_04_amd.runner import DeviceCase
+    from workloads import make_case
+
+    prefix, H, rows, crossover = 8192, 128, [], None
+    for q in (64, 128, 256, 512, 1024, 2048):
+        case = make_case(f"crossover q={q}", 300 + q, H, [prefix + q] * 2, q_lens=[q] * 2)
+        dc = DeviceCase(case)
+        dc.fill_history()
+        dc.prepare_step_inputs()
+        dc.append_new()
+        dc.alloc_prefill()
+        dc.alloc_prefill_expanded()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dc.prefill()
+            dc.prefill_expanded()
+        n = max(3, min(args.steps, 10))
+        ms_a = time_each(torch, lambda i: dc.prefill(), n)
+        ms_x = time_each(torch, lambda i: dc.prefill_expanded(), n)
+        rows.append({"q_per_seq": q, "absorbed_ms": round(ms_a, 4), "expanded_ms": round(ms_x, 4),
+                     "expanded_speedup": round(ms_a / ms_x, 3)})
+        if crossover is None and ms_x < ms_a:
+            crossover = q
+        del dc
+        torch.cuda.empty_cache()
+    result = {
+        "metric": "chunked prefill crossover: shortest chunk at which the expanded form beats the absorbed form",
+        "value": crossover, "unit": "query tokens per sequence", "n_gpus": 1, "steps": max(3, min(args.steps, 10)),
+        "warmup": 2, "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"chunked prefill B=2 n_h={H}, {prefix} cached + chunk q, causal", "prefix": prefix},
+        "sweep": rows, "device": props.name,
+    }
     print(json.dumps(result), flush=True)
 
 
