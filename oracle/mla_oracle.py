@@ -37,6 +37,9 @@ Readings where the pages leave a step open (each is also listed in the design no
     keys 0..L-1. Prefill: query at position p sees keys 0..p (causal).
   * lse is the natural-log log-sum-exp of the scaled scores.
   * bf16 rounding is round-to-nearest-even.
+  * Query path: q_lora_rank = 512 (the module's default in [P1] section 2); wq_b's output per head
+    is [q_nope | q_R]; W_UQK[h] = W_UK[h]^T W_UQ_nope[h] is rounded once to bf16; q_R is rounded,
+    then rotated and rounded again.
   * KV down-projection: wkv_a's output is rounded to bf16 before the split (the Linear's output
     dtype); RMSNorm is computed in float64 with the caller's eps and rounded once.
 """
@@ -195,6 +198,49 @@ def kv_down_append(cache: np.ndarray, block_table, max_blocks: int, token_seq, t
     c, kr = kv_down(x, w_dkv, gamma, eps)
     cache, _ = rope_append(cache, block_table, max_blocks, token_seq, token_pos, c, kr, None, theta)
     return cache
+
+
+# ----------------------------------------------------------------------------- query path
+
+def q_down(x: np.ndarray, w_dq: np.ndarray, gamma_q: np.ndarray, eps: float) -> np.ndarray:
+    """The compressed query c_q = q_norm(wq_a(x)) ([P1] section 2 forward: wq_a, then the RMSNorm
+    q_norm over q_lora_rank values). x [T, dim], w_dq [q_rank, dim], gamma_q [q_rank] bf16 bits;
+    the projection is rounded to bf16 (the Linear's output dtype), normalised in float64 and rounded
+    again. Returns c_q [T, q_rank] bf16 bits."""
+    cq = f64_to_bf16(bf16_to_f64(x) @ bf16_to_f64(w_dq).T)
+    return f64_to_bf16(rms_norm(bf16_to_f64(cq), bf16_to_f64(gamma_q), eps))
+
+
+def q_up_split(w_uq: np.ndarray, n_heads: int, d_nope: int):
+    """wq_b's rows per head: its output is viewed as [n_heads, d_nope + d_R] and split into q_nope
+    and q_R in that order ([P1] section 2). w_uq [n_heads (d_nope + d_R), q_rank] ->
+    (W_UQ_nope [H, d_nope, q_rank], W_QR [H, d_R, q_rank])."""
+    w = np.asarray(w_uq).reshape(n_heads, -1, np.asarray(w_uq).shape[-1])
+    return w[:, :d_nope, :], w[:, d_nope:, :]
+
+
+def absorb_query_weights(w_uq_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """W_UQK[h] = W_UK[h]^T W_UQ_nope[h] ([d_c, q_rank] per head), the query and key projections
+    multiplied ahead of time ([P3] "MLA的數學原理": the score x_t (W_q W_k^T) c_i^T; [P1] section 4:
+    the absorbed query is scored directly against c_KV). The fp64 product is rounded once to bf16."""
+    return f64_to_bf16(np.einsum("hdc,hdr->hcr", bf16_to_f64(w_uk), bf16_to_f64(w_uq_nope)))
+
+
+def query_rows(c_q: np.ndarray, pos, w_uqk: np.ndarray, w_qr: np.ndarray, theta: float = ROPE_THETA) -> np.ndarray:
+    """The absorbed query rows from the compressed query: [T, H, d_c + d_R] bf16 bits,
+    [W_UQK[h] c_q | R_pos (W_QR[h] c_q)]. The latent part is one rounding of the fp64 product; q_R
+    is rounded (wq_b's output), turned by the token's position in fp64 and rounded again, as the
+    plain RoPE step does for a query."""
+    cq = bf16_to_f64(c_q)
+    q_abs = f64_to_bf16(np.einsum("hcr,tr->thc", bf16_to_f64(w_uqk), cq))
+    q_r = f64_to_bf16(np.einsum("hdr,tr->thd", bf16_to_f64(w_qr), cq))
+    q_r = f64_to_bf16(rope_rotate(bf16_to_f64(q_r), np.asarray(pos)[:, None], theta))
+    return np.concatenate([q_abs, q_r], axis=-1)
+
+
+def query_absorbed(x, pos, w_dq, gamma_q, eps: float, w_uqk, w_qr, theta: float = ROPE_THETA) -> np.ndarray:
+    """query_rows(q_down(x)): the decode kernel's query input straight from the hidden state."""
+    return query_rows(q_down(x, w_dq, gamma_q, eps), pos, w_uqk, w_qr, theta)
 
 
 def gather_rows(cache: np.ndarray, block_table, max_blocks: int, seq: int, length: int) -> np.ndarray:

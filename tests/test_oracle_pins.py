@@ -381,10 +381,48 @@ def pin_kv_down():
         assert np.array_equal(cache[b * 2 + p // 4, p % 4, d_c:], rot)
 
 
+def pin_query_path():
+    # W_DQ and W_UQ rows that pick single input coordinates make every projection exact, so each
+    # part of the query path is checked against an already pinned routine
+    rng = np.random.default_rng(8)
+    H, d_nope, d_r, d_c, r, dim, T = 2, 3, 4, 5, 6, 10, 3
+    x = bf16_bits(rng.standard_normal((T, dim)))
+    pick_q = rng.permutation(dim)[:r]
+    w_dq = np.zeros((r, dim))
+    w_dq[np.arange(r), pick_q] = 1.0
+    gamma = bf16_bits(1.0 + 0.25 * rng.standard_normal(r))
+    cq = O.q_down(x, bf16_bits(w_dq), gamma, 1e-6)
+    assert np.array_equal(cq, O.f64_to_bf16(O.rms_norm(O.bf16_to_f64(x)[:, pick_q], O.bf16_to_f64(gamma), 1e-6)))
+    # wq_b: head h's rows are [nope (d_nope) | rope (d_r)], each picking one coordinate of c_q
+    # distinct picks per head: every entry of W_UK[h]^T W_UQ_nope[h] is then one W_UK entry (exact)
+    pick_n = np.stack([rng.permutation(r)[:d_nope] for _ in range(H)])
+    pick_r = rng.integers(0, r, (H, d_r))
+    w_uq = np.zeros((H, d_nope + d_r, r))
+    for h in range(H):
+        w_uq[h, np.arange(d_nope), pick_n[h]] = 1.0
+        w_uq[h, d_nope + np.arange(d_r), pick_r[h]] = 1.0
+    w_uq = bf16_bits(w_uq.reshape(H * (d_nope + d_r), r))
+    wn, wr = O.q_up_split(w_uq, H, d_nope)
+    assert wn.shape == (H, d_nope, r) and wr.shape == (H, d_r, r)
+    w_uk = bf16_bits(rng.standard_normal((H, d_nope, d_c)))
+    w_uqk = O.absorb_query_weights(wn, w_uk)
+    assert w_uqk.shape == (H, d_c, r)
+    pos = np.array([0, 7, 130])
+    rows = O.query_rows(cq, pos, w_uqk, wr)
+    # the latent part equals the absorption of q_nope = c_q[pick_n] through W_UK (absorb_query)
+    q_nope = np.stack([cq[:, pick_n[h]] for h in range(H)], axis=1)
+    q_rope = np.stack([cq[:, pick_r[h]] for h in range(H)], axis=1)
+    want = O.absorb_query(q_nope, q_rope, w_uk)
+    assert np.array_equal(rows[..., :d_c], O.f64_to_bf16(want[..., :d_c]))
+    # the RoPE part is c_q[pick_r] turned by the position
+    assert np.array_equal(rows[..., d_c:], O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(q_rope), pos[:, None])))
+    assert np.array_equal(O.query_absorbed(x, pos, bf16_bits(w_dq), gamma, 1e-6, w_uqk, wr), rows)
+
+
 PINS = [pin_bf16_rounding, pin_rope_complex_form, pin_rope_invariants, pin_bruteforce_decode,
         pin_bruteforce_prefill, pin_absorbed_equals_expanded, pin_special_cases, pin_wuk_zero_matches_sdpa,
         pin_split_invariance, pin_prefill_equals_decodes, pin_slot_mapping, pin_closed_forms, pin_rms_norm,
-        pin_kv_down]
+        pin_kv_down, pin_query_path]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -467,7 +505,19 @@ def _mut_kv_split_swapped(monkeypatch):
     monkeypatch.setattr(O, "kv_split", lambda kv, d_c: (kv[..., kv.shape[-1] - d_c:], kv[..., :kv.shape[-1] - d_c]))
 
 
+def _mut_q_split_swapped(monkeypatch):
+    orig = O.q_up_split
+    monkeypatch.setattr(O, "q_up_split", lambda w, n, d: tuple(reversed(orig(w, n, w.shape[0] // n - d))))
+
+
+def _mut_uqk_transposed(monkeypatch):
+    monkeypatch.setattr(O, "absorb_query_weights", lambda wn, wk: O.f64_to_bf16(
+        np.einsum("hdc,hdr->hrc", O.bf16_to_f64(wk), O.bf16_to_f64(wn))))
+
+
 MUTANTS = [
+    (_mut_q_split_swapped, [pin_query_path]),
+    (_mut_uqk_transposed, [pin_query_path]),
     (_mut_rms_sum, [pin_rms_norm]),
     (_mut_kv_split_swapped, [pin_kv_down]),
     (_mut_rope_sign, [pin_rope_complex_form]),
