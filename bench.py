@@ -45,11 +45,14 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "prefill", "prefill_crossover", "kv_down"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "prefill_crossover", "kv_down", "query"],
+                    default="decode",
                     help="decode: B=32, n_h=128, 4K context (the headline); prefill: chunked prefill, 2 x 1024 "
                          "new tokens after 8192 cached; prefill_crossover: absorbed against expanded prefill over "
                          "chunk lengths 64..2048 after 8192 cached; kv_down: KV down-projection + kv_norm + RoPE "
-                         "append of the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096")
+                         "append of the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096; "
+                         "query: the absorbed query rows of the decode step's 32 tokens straight from the hidden "
+                         "state (W_UQ W_UK multiplied ahead of time), width 4096, rank 512")
     return ap.parse_args()
 
 
@@ -162,6 +165,8 @@ def main():
         return kv_down_main(args, torch, lib, props)
     if args.workload == "prefill_crossover":
         return crossover_main(args, torch, lib, props)
+    if args.workload == "query":
+        return query_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -458,6 +463,84 @@ def crossover_main(args, torch, lib, props):
 
 KV_DIM = 4096
 KV_EPS = 1e-6
+Q_RANK = 512
+
+
+def query_bytes(T, H, dim, r):
+    """Algorithmic HBM bytes of one mla_query_absorbed call: the prepared weight (W_UQK and the q_R rows),
+    W_DQ, q_norm's weight, x and positions in; the absorbed rows out."""
+    return H * 512 * r * 2 + H * 64 * r * 2 + r * dim * 2 + r * 2 + T * dim * 2 + T * 4 + T * H * 576 * 2
+
+
+def query_main(args, torch, lib, props):
+    from workloads import make_query_inputs
+    T, H, r = 32, 128, Q_RANK
+    dims = lib.make_dims(H)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to("cuda")
+    sets = []
+    for k in range(4):  # 4 x 80 MB of weights: more than the Infinity Cache holds
+        inp = make_query_inputs(500 + k, T, KV_DIM, H, r)
+        st = {"pos": dev(np.full(T, 4095, np.int32), np.int32), "x": dev(inp.x, np.int16),
+              "w_dq": dev(inp.w_dq, np.int16), "g": dev(inp.gamma_q, np.int16), "w_uq": dev(inp.w_uq, np.int16),
+              "w_uk": dev(inp.w_uk, np.int16)}
+        st["w_q"] = torch.empty(H * 576 * r, dtype=torch.int16, device="cuda")
+        lib.absorb_query_weights(dims, st["w_uq"], st["w_uk"], st["w_q"])
+        st["ws"] = torch.empty(lib.query_absorbed_workspace_size(dims, T, KV_DIM, r), dtype=torch.uint8,
+                               device="cuda")
+        st["q"] = torch.empty((T, H, 576), dtype=torch.int16, device="cuda")
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    def run(i):
+        st = sets[i % len(sets)]
+        lib.query_absorbed(dims, st["pos"], st["x"], st["w_dq"], st["g"], KV_EPS, st["w_q"], st["ws"], st["q"])
+
+    def prep(i):
+        st = sets[i % len(sets)]
+        lib.absorb_query_weights(dims, st["w_uq"], st["w_uk"], st["w_q"])
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ms = time_each(torch, run, args.steps)
+    ms_b2b = time_loop(torch, run, args.steps)
+    ms_prep = time_each(torch, prep, 4)
+    nbytes = query_bytes(T, H, KV_DIM, r)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    two_step = H * 192 * r * 2 + H * 128 * 512 * 2  # W_UQ and W_UK, had the product not been taken ahead of time
+    result = {
+        "metric": "absorbed query rows from the hidden state (W_UQ W_UK pre-multiplied) GB/s, 32 decode tokens",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "ms_back_to_back": round(ms_b2b, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"mla_query_absorbed T={T} n_h={H} dim={KV_DIM} q_rank={r} (positions 4095)",
+                   "num_tokens": T, "n_heads": H, "dim": KV_DIM, "q_rank": r, "input_sets_rotated": len(sets)},
+        "roofline": {"kernel": "mla_query_absorbed (splitk_gemm_kernel + cq_finish_kernel + query_gemm_kernel)",
+                     "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "weight_bytes": {"pre_multiplied": H * 512 * r * 2 + H * 64 * r * 2, "two_step_W_UQ_and_W_UK": two_step},
+        "weight_prep_ms": round(ms_prep, 4),
+        "device": props.name,
+    }
+    if not args.no_cpu:
+        from oracle import mla_oracle as O
+        inp = make_query_inputs(500, T, KV_DIM, H, r)
+        wn, wr = O.q_up_split(inp.w_uq, H, 128)
+        w_uqk = O.absorb_query_weights(wn, inp.w_uk)
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            O.query_absorbed(inp.x, np.full(T, 4095), inp.w_dq, inp.gamma_q, KV_EPS, w_uqk, wr)
+            reps += 1
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+                                  "kind": "oracle", "sample": f"{reps} repetitions of the whole 32-token call "
+                                                              f"(weights prepared outside the timing), fp64, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
 
 
 class KvDownSet:

@@ -229,6 +229,86 @@ __global__ void __launch_bounds__(256) gemm_bt_partial_kernel(int M, int N, int 
       }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Split-K GEMM for few rows (M up to a few hundred): part[s][m][n] = sum over split s of A[m][k] B[n][k].
+// Work-group (column tile of 32, split s, block of 32 rows): wave w takes a quarter of the split's K
+// range with v_mfma_f32_32x32x16_bf16 straight from global memory (both operands K-contiguous), two
+// K steps of operands in flight; the four partial tiles are added through LDS. Many splits spread
+// the weight B over many work-groups, so it streams from HBM once at full width.
+constexpr int kKStep = 16;  // K per MFMA
+constexpr int kAhead = 2;   // K steps whose operands are loaded ahead
+
+__global__ void __launch_bounds__(256) splitk_gemm_kernel(int M, int N, int K, int split_len,
+                                                          const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ B,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4 * 32 * 32];
+  const int ct = blockIdx.x, s = blockIdx.y, tb = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int quarter = split_len / 4;
+  const int k0 = s * split_len + wave * quarter;
+  const int steps = quarter / kKStep;
+  // A: row 32 tb + lane % 32 (clamped; rows past the end are computed and not stored), K half lane / 32
+  const int row = min(32 * tb + (lane & 31), M - 1);
+  const uint16_t* pa = A + (int64_t)row * K + k0 + 8 * (lane >> 5);
+  // B: output column 32 ct + lane % 32, the same K half
+  const uint16_t* pb = B + (int64_t)(32 * ct + (lane & 31)) * K + k0 + 8 * (lane >> 5);
+  bf16x8 a[kAhead], b[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    if (i < steps) {
+      a[i] = *reinterpret_cast<const bf16x8*>(pa + i * kKStep);
+      b[i] = *reinterpret_cast<const bf16x8*>(pb + i * kKStep);
+    }
+  }
+  f32x16 acc = f32x16{};
+  for (int k = 0; k < steps; k += kAhead) {
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      if (k + i < steps) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], acc, 0, 0, 0);
+        if (k + i + kAhead < steps) {
+          a[i] = *reinterpret_cast<const bf16x8*>(pa + (k + i + kAhead) * kKStep);
+          b[i] = *reinterpret_cast<const bf16x8*>(pb + (k + i + kAhead) * kKStep);
+        }
+      }
+    }
+  }
+  // D: lane holds row 8 (j / 4) + 4 (lane / 32) + j % 4 and column lane % 32 of the tile
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int m = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+    red[(wave * 32 + m) * 32 + (lane & 31)] = acc[j];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+    const int m = e >> 5, n = e & 31;
+    const int t = 32 * tb + m;
+    if (t < M) part[((int64_t)s * M + t) * N + 32 * ct + n] = red[e] + red[1024 + e] + red[2048 + e] + red[3072 + e];
+  }
+}
+
+int splitk_splits(int M, int N, int K) {
+  // enough work-groups (column tiles x splits x row blocks) to spread B over the chip, each split a
+  // multiple of 64 (four waves x 16) and at least 256 long
+  const int tblocks = (M + 31) / 32;
+  int ns = 512 / std::max(1, (N / 32) * tblocks);
+  ns = std::max(1, std::min(std::min(ns, kGemmMaxSplits), K / 256));
+  while ((K / 64) % ns != 0) --ns;
+  return ns;
+}
+
+hipError_t launch_splitk_gemm(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
+                              hipStream_t stream) {
+  if (M <= 0 || N % 32 != 0 || K % 64 != 0 || nsplit < 1 || (K / 64) % nsplit != 0) return hipErrorInvalidValue;
+  const int tblocks = (M + 31) / 32;
+  if (tblocks > 65535 || nsplit > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitk_gemm_kernel, dim3(N / 32, nsplit, tblocks), dim3(256), 0, stream, M, N, K, K / nsplit, A, B,
+                     part);
+  return hipGetLastError();
+}
+
 int gemm_bt_splits(int M, int N, int K) {
   const int tiles = ((M + kGemmBM - 1) / kGemmBM) * (N / kGemmBN);
   int ns = std::max(1, 256 / std::max(1, tiles));

@@ -5,8 +5,8 @@
 //
 // Two kernels:
 //   1. kv = x . W_DKV^T with bf16 MFMA, fp32 accumulation, as fp32 partials over splits of the input
-//      dimension. From 256 tokens on, the tiled GEMM of gemm_bt.hip; below, kv_down_gemm_kernel,
-//      split so that the weight (d_c + d_R rows of `dim`) streams through many work-groups:
+//      dimension. From 256 tokens on, the tiled GEMM of gemm_bt.hip; below, its split-K kernel,
+//      split so that the weight (d_c + d_R rows of `dim`) streams through many work-groups.
 //      Work-group (column tile of 32, split s, block of 32 tokens): wave w takes a quarter of the
 //      split's K range; the four partial tiles are added through LDS and written as fp32 partials
 //      [split][token][576]. Both MFMA operands are K-contiguous in memory (x rows; W_DKV rows in the
@@ -27,83 +27,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRowOut = kDc + kDr;  // 576 outputs per token
-constexpr int kColTiles = kRowOut / 32;
-constexpr int kKStep = 16;          // K per MFMA
-constexpr int kAhead = 2;           // K steps whose operands are loaded ahead
 constexpr int kMaxSplits = kGemmMaxSplits;  // splits of the input dimension
 
 // Token counts from here on take the tiled GEMM (128 x 192 tiles, operands through LDS); fewer
-// tokens take kv_down_gemm_kernel, which spreads the weight over many work-groups.
+// tokens take the split-K kernel of gemm_bt.hip, which spreads the weight over many work-groups.
 constexpr int kTiledMinTokens = 256;
 
 inline bool kv_down_tiled(int num_tokens) { return num_tokens >= kTiledMinTokens; }
 
 inline int kv_down_splits(int num_tokens, int dim) {
   if (kv_down_tiled(num_tokens)) return gemm_bt_splits(num_tokens, kRowOut, dim);
-  // enough work-groups (column tiles x splits x token blocks) to spread the weight over the chip,
-  // each split a multiple of 64 (four waves x 16)
-  const int tblocks = (num_tokens + 31) / 32;
-  int ns = 512 / (kColTiles * tblocks);
-  ns = std::max(1, std::min(std::min(ns, kMaxSplits), dim / 256));
-  while ((dim / 64) % ns != 0) --ns;
-  return ns;
+  return splitk_splits(num_tokens, kRowOut, dim);
 }
 }  // namespace
 
 size_t kv_down_workspace_bytes(int num_tokens, int dim) {
   return (size_t)kv_down_splits(num_tokens, dim) * num_tokens * kRowOut * 4;
-}
-
-__global__ void __launch_bounds__(256) kv_down_gemm_kernel(int num_tokens, int dim, int split_len,
-                                                           const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ w_dkv,
-                                                           float* __restrict__ part) {
-  __shared__ float red[4 * 32 * 32];
-  const int ct = blockIdx.x, s = blockIdx.y, tb = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int quarter = split_len / 4;
-  const int k0 = s * split_len + wave * quarter;
-  const int steps = quarter / kKStep;
-  // A: token 32 tb + lane % 32 (clamped; rows past the end are computed and not stored), K half lane / 32
-  const int tok = min(32 * tb + (lane & 31), num_tokens - 1);
-  const uint16_t* xa = x + (int64_t)tok * dim + k0 + 8 * (lane >> 5);
-  // B: output column 32 ct + lane % 32, the same K half
-  const uint16_t* wb = w_dkv + (int64_t)(32 * ct + (lane & 31)) * dim + k0 + 8 * (lane >> 5);
-  bf16x8 a[kAhead], b[kAhead];
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) {
-    if (i < steps) {
-      a[i] = *reinterpret_cast<const bf16x8*>(xa + i * kKStep);
-      b[i] = *reinterpret_cast<const bf16x8*>(wb + i * kKStep);
-    }
-  }
-  f32x16 acc = f32x16{};
-  for (int k = 0; k < steps; k += kAhead) {
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) {
-      if (k + i < steps) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], acc, 0, 0, 0);
-        if (k + i + kAhead < steps) {
-          a[i] = *reinterpret_cast<const bf16x8*>(xa + (k + i + kAhead) * kKStep);
-          b[i] = *reinterpret_cast<const bf16x8*>(wb + (k + i + kAhead) * kKStep);
-        }
-      }
-    }
-  }
-  // D: lane holds token 8 (j / 4) + 4 (lane / 32) + j % 4 and column lane % 32 of the tile
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int m = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-    red[(wave * 32 + m) * 32 + (lane & 31)] = acc[j];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-    const int m = e >> 5, n = e & 31;
-    const int t = 32 * tb + m;
-    if (t < num_tokens)
-      part[((int64_t)s * num_tokens + t) * kRowOut + 32 * ct + n] = red[e] + red[1024 + e] + red[2048 + e] + red[3072 + e];
-  }
 }
 
 __global__ void __launch_bounds__(256) kv_down_finish_kernel(CacheView cache, int num_tokens, int nsplit,
@@ -181,9 +120,7 @@ hipError_t launch_kv_down(const CacheView& cache, int num_tokens, const int32_t*
   if (kv_down_tiled(num_tokens)) {
     e = launch_gemm_bt_partial(num_tokens, kRowOut, dim, ns, x, w_dkv, part, stream);
   } else {
-    hipLaunchKernelGGL(kv_down_gemm_kernel, dim3(kColTiles, ns, tblocks), dim3(256), 0, stream, num_tokens, dim,
-                       dim / ns, x, w_dkv, part);
-    e = hipGetLastError();
+    e = launch_splitk_gemm(num_tokens, kRowOut, dim, ns, x, w_dkv, part, stream);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kv_down_finish_kernel, dim3(num_tokens), dim3(256), 0, stream, cache, num_tokens, ns, token_seq,

@@ -84,6 +84,43 @@ int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_to
                                           q_rope_inout, dims->rope_theta, stream));
 }
 
+int mla_absorb_query_weights(const mla_dims* dims, int32_t q_rank, const uint16_t* w_uq, const uint16_t* w_uk,
+                             uint16_t* w_q, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (q_rank <= 0) return MLA_ERR_BAD_ARG;
+  if (q_rank % 64 != 0 || q_rank > 2048) return MLA_ERR_UNSUPPORTED;
+  if (!w_uq || !w_uk || !w_q) return MLA_ERR_NULL;
+  if (((uintptr_t)w_q & 7) != 0 || ((uintptr_t)w_uq & 7) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_absorb_query_weights(dims->n_heads, q_rank, w_uq, w_uk, w_q, stream));
+}
+
+size_t mla_query_absorbed_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim, int32_t q_rank) {
+  if (check_dims(dims) != MLA_OK || num_tokens < 0 || dim <= 0 || dim % 64 != 0 || q_rank <= 0 || q_rank % 64 != 0 ||
+      q_rank > 2048)
+    return 0;
+  return mla::query_workspace_bytes(num_tokens, dim, q_rank);
+}
+
+int mla_query_absorbed(const mla_dims* dims, int32_t num_tokens, const int32_t* token_pos, const uint16_t* x,
+                       int32_t dim, const uint16_t* w_dq, const uint16_t* gamma_q, float eps, int32_t q_rank,
+                       const uint16_t* w_q, void* workspace, size_t workspace_bytes, uint16_t* q_abs,
+                       hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535 * 32 || dim <= 0 || q_rank <= 0) return MLA_ERR_BAD_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return MLA_ERR_BAD_ARG;
+  if (dim % 64 != 0 || q_rank % 64 != 0 || q_rank > 2048) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MLA_OK;
+  if (!token_pos || !x || !w_dq || !gamma_q || !w_q || !workspace || !q_abs) return MLA_ERR_NULL;
+  if (workspace_bytes < mla::query_workspace_bytes(num_tokens, dim, q_rank)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0 || ((uintptr_t)x & 15) != 0 || ((uintptr_t)w_dq & 15) != 0 ||
+      ((uintptr_t)w_q & 15) != 0 || ((uintptr_t)q_abs & 7) != 0)
+    return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_query_absorbed(dims->n_heads, num_tokens, token_pos, x, dim, w_dq, gamma_q, eps, q_rank,
+                                             w_q, dims->rope_theta, workspace, q_abs, stream));
+}
+
 size_t mla_chunked_prefill_expanded_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_seq_len) {
   if (check_dims(dims) != MLA_OK || batch < 0 || max_seq_len < 0) return 0;
   return mla::prefill_expanded_kv_bytes(batch, dims->n_heads, max_seq_len);

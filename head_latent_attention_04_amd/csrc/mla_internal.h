@@ -104,6 +104,25 @@ int gemm_bt_splits(int M, int N, int K);
 hipError_t launch_gemm_bt_partial(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
                                   hipStream_t stream);
 
+// Split-K GEMM for few rows, fp32 partials: part[s][m][n] = sum_{k in split s} A[m][k] B[n][k]
+// (A [M, K], B [N, K] row-major bf16; N % 32 == 0, K % 64 == 0, nsplit divides K / 64).
+int splitk_splits(int M, int N, int K);
+hipError_t launch_splitk_gemm(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
+                              hipStream_t stream);
+
+// Query path with W_UQ W_UK absorbed ahead of time: the prepared weight w_q = head h's rows
+// [W_UQK[h] = W_UK[h]^T W_UQ_nope[h] (512 rows); W_QR[h] (64 rows)] in MFMA operand order
+// ([n_heads, 576, q_rank] elements), from wq_b's weight W_UQ [n_heads (128 + 64), q_rank] and W_UK;
+// then the absorbed query rows [T, n_heads, 576] (plain layout) from x [T, dim]:
+// c_q = RMSNorm(x W_DQ^T), [W_UQK[h] c_q | RoPE(W_QR[h] c_q)].
+hipError_t launch_absorb_query_weights(int n_heads, int q_rank, const uint16_t* w_uq, const uint16_t* w_uk,
+                                       uint16_t* w_q, hipStream_t stream);
+size_t query_workspace_bytes(int num_tokens, int dim, int q_rank);
+hipError_t launch_query_absorbed(int n_heads, int num_tokens, const int32_t* token_pos, const uint16_t* x, int dim,
+                                 const uint16_t* w_dq, const uint16_t* gamma_q, float eps, int q_rank,
+                                 const uint16_t* w_q, float theta, void* workspace, uint16_t* q_abs,
+                                 hipStream_t stream);
+
 // Expanded-form chunked prefill: up-projected keys and values ([batch, n_heads, lpad, 128] each,
 // lpad = max_seq_len rounded up to 128, in the workspace), then causal attention with 192-wide keys.
 size_t prefill_expanded_kv_bytes(int batch, int n_heads, int max_seq_len);

@@ -44,6 +44,10 @@ EXPORTS = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_rope_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp,
                                        _vp, _vp]),
+    "mla_absorb_query_weights": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp, _vp]),
+    "mla_query_absorbed_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32, _i32]),
+    "mla_query_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
+                                          _i32, _vp, _vp, _sz, _vp, _vp]),
     "mla_chunked_prefill_expanded_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32]),
     "mla_chunked_prefill_expanded": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp,
                                                     _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
@@ -145,6 +149,35 @@ def rope_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_ro
         _ptr(k_rope, "k_rope", BF16, T * dims.d_rope),
         _ptr(q_rope, "q_rope", BF16, T * dims.n_heads * dims.d_rope), _stream(stream))
     _check("mla_rope_append", st)
+
+
+def absorb_query_weights(dims: MlaDims, w_uq, w_uk, w_q, stream=None):
+    """w_q: the prepared query weight, n_heads * 576 * q_rank bf16 in MFMA operand order."""
+    H = dims.n_heads
+    r = w_uq.shape[-1] if w_uq.dim() == 2 else 0
+    st = load().mla_absorb_query_weights(
+        ctypes.byref(dims), r, _ptr(w_uq, "w_uq", BF16, H * (dims.d_nope + dims.d_rope) * r),
+        _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c),
+        _ptr(w_q, "w_q", BF16, H * (dims.d_c + dims.d_rope) * r), _stream(stream))
+    _check("mla_absorb_query_weights", st)
+
+
+def query_absorbed_workspace_size(dims: MlaDims, num_tokens: int, dim: int, q_rank: int) -> int:
+    return int(load().mla_query_absorbed_workspace_size(ctypes.byref(dims), num_tokens, dim, q_rank))
+
+
+def query_absorbed(dims: MlaDims, token_pos, x, w_dq, gamma_q, eps: float, w_q, workspace, q_abs, stream=None):
+    T = token_pos.numel()
+    H = dims.n_heads
+    dim = x.shape[1] if x.dim() == 2 else 0
+    r = w_dq.shape[0] if w_dq.dim() == 2 else 0
+    st = load().mla_query_absorbed(
+        ctypes.byref(dims), T, _ptr(token_pos, "token_pos", I32, T), _ptr(x, "x", BF16, T * dim), dim,
+        _ptr(w_dq, "w_dq", BF16, r * dim), _ptr(gamma_q, "gamma_q", BF16, r), eps, r,
+        _ptr(w_q, "w_q", BF16, H * (dims.d_c + dims.d_rope) * r),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(q_abs, "q_abs", BF16, T * H * (dims.d_c + dims.d_rope)), _stream(stream))
+    _check("mla_query_absorbed", st)
 
 
 def chunked_prefill_expanded_workspace_size(dims: MlaDims, batch: int, max_seq_len: int) -> int:

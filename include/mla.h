@@ -244,6 +244,42 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
                         size_t workspace_bytes, uint16_t* out, float* lse_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * The query path with the query and key projections multiplied ahead of time
+ * ("论文复现工坊 No.4", section 2: wq_a, q_norm (RMSNorm over q_lora_rank), wq_b with per-head
+ * output [q_nope (d_nope) | q_R (d_rope)]; section 4: the absorbed query is scored against c_KV;
+ * "淺析DeepSeek多頭潛在注意力機制（MLA）", "MLA的數學原理": the product of the query and key
+ * projections formed once).
+ *
+ * mla_absorb_query_weights - once per weight set: the prepared query weight w_q, head h's 576 rows
+ *   [W_UQK[h] = W_UK[h]^T W_UQ_nope[h] (d_c rows, fp32 sums, one rounding); W_QR[h] (d_rope rows, copied)]
+ *   of q_rank elements each, stored in MFMA operand order: row n, element k of head h at
+ *     (((h * 18 + n / 32) * (q_rank / 16) + k / 16) * 64 + n % 32 + 32 ((k / 8) % 2)) * 8 + k % 8
+ *   (n_heads * 576 * q_rank bf16 in all, 8-byte aligned).
+ *   w_uq  [n_heads (d_nope + d_rope), q_rank] bf16 (wq_b's weight; head h's rows are its q_nope rows,
+ *         then its q_R rows), 8-byte aligned;  w_uk [n_heads, d_nope, d_c] bf16 as for decode.
+ *   q_rank a positive multiple of 64 up to 2048 (else MLA_ERR_UNSUPPORTED).
+ *
+ * mla_query_absorbed - the decode kernel's query rows straight from the hidden state:
+ *   c_q = bf16(RMSNorm(bf16(x W_DQ^T)) with eps and gamma_q)
+ *   q_abs[t, h, 0:d_c]   = bf16(W_UQK[h] c_q[t])
+ *   q_abs[t, h, d_c:576] = R_pos(t) bf16(W_QR[h] c_q[t])   (fp64 angles as mla_rope_append, one rounding)
+ *   x [num_tokens, dim] bf16, dim a multiple of 64;  w_dq [q_rank, dim];  gamma_q [q_rank]
+ *   w_q the prepared weight of mla_absorb_query_weights;  token_pos [num_tokens] int32;
+ *   q_abs [num_tokens, n_heads, 576] bf16 (the layout mla_decode_absorbed takes);
+ *   workspace >= mla_query_absorbed_workspace_size(...) bytes, 256-byte aligned;  x, w_dq, w_q
+ *   16-byte aligned, q_abs 8-byte aligned.
+ * Three launches on `stream`; num_tokens == 0 is a no-op. The size query returns 0 for arguments
+ * the call would reject.
+ * ------------------------------------------------------------------------------------------- */
+int mla_absorb_query_weights(const mla_dims* dims, int32_t q_rank, const uint16_t* w_uq, const uint16_t* w_uk,
+                             uint16_t* w_q, hipStream_t stream);
+size_t mla_query_absorbed_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim, int32_t q_rank);
+int mla_query_absorbed(const mla_dims* dims, int32_t num_tokens, const int32_t* token_pos, const uint16_t* x,
+                       int32_t dim, const uint16_t* w_dq, const uint16_t* gamma_q, float eps, int32_t q_rank,
+                       const uint16_t* w_q, void* workspace, size_t workspace_bytes, uint16_t* q_abs,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mla_chunked_prefill_expanded - the same causal chunked prefill as mla_chunked_prefill, computed in
  * the expanded form ("Multi-Head Latent Attention: DeepSeek V2/V3 工程视角" names the up-projection
  * of the latent cache and its absorbed equivalent as the two ways to attend; "论文复现工坊 No.4",

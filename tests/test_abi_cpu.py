@@ -146,3 +146,36 @@ def test_kv_down_validation_and_workspace():
     assert lib.kv_down_append_workspace_size(d, 20000, 4096) == 20000 * 576 * 4
     assert lib.kv_down_append_workspace_size(d, 32, 100) == 0
     assert lib.kv_down_append_workspace_size(d, -1, 4096) == 0
+
+
+def qabs(dims, T=1, dim=4096, eps=1e-6, r=512, ptrs=(FAKE,) * 5, ws=FAKE, wsb=1 << 40, out=FAKE):
+    return lib.load().mla_query_absorbed(ctypes.byref(dims), T, ptrs[0], ptrs[1], dim, ptrs[2], ptrs[3], eps, r,
+                                         ptrs[4], ws, wsb, out, None)
+
+
+def test_query_path_validation_and_workspace():
+    d = D()
+    L = lib.load()
+    assert L.mla_absorb_query_weights(ctypes.byref(d), 100, FAKE, FAKE, FAKE, None) == lib.MLA_ERR_UNSUPPORTED
+    assert L.mla_absorb_query_weights(ctypes.byref(d), 0, FAKE, FAKE, FAKE, None) == lib.MLA_ERR_BAD_ARG
+    assert L.mla_absorb_query_weights(ctypes.byref(d), 4096, FAKE, FAKE, FAKE, None) == lib.MLA_ERR_UNSUPPORTED
+    assert L.mla_absorb_query_weights(ctypes.byref(d), 512, None, FAKE, FAKE, None) == lib.MLA_ERR_NULL
+    assert L.mla_absorb_query_weights(ctypes.byref(D(n_heads=120)), 512, FAKE, FAKE, FAKE, None) \
+        == lib.MLA_ERR_UNSUPPORTED
+    assert qabs(d, dim=100) == lib.MLA_ERR_UNSUPPORTED
+    assert qabs(d, r=100) == lib.MLA_ERR_UNSUPPORTED
+    assert qabs(d, T=-1) == lib.MLA_ERR_BAD_ARG
+    assert qabs(d, dim=0) == lib.MLA_ERR_BAD_ARG
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert qabs(d, eps=eps) == lib.MLA_ERR_BAD_ARG
+    assert qabs(d, ptrs=(FAKE, None, FAKE, FAKE, FAKE)) == lib.MLA_ERR_NULL
+    assert qabs(d, ptrs=(FAKE, FAKE, FAKE, FAKE, None)) == lib.MLA_ERR_NULL
+    assert qabs(d, out=None) == lib.MLA_ERR_NULL
+    assert qabs(d, wsb=1000) == lib.MLA_ERR_BAD_ARG
+    assert qabs(d, ws=FAKE + 16) == lib.MLA_ERR_BAD_ARG
+    assert qabs(d, out=FAKE + 2) == lib.MLA_ERR_BAD_ARG
+    assert qabs(d, T=0, ptrs=(None,) * 5, ws=None, wsb=0, out=None) == lib.MLA_OK
+    # 32 tokens, width 4096, rank 512: fp32 partials of 16 splits, c_q (one 32-token block), and 32
+    # cos/sin pairs per token
+    assert lib.query_absorbed_workspace_size(d, 32, 4096, 512) == 16 * 32 * 512 * 4 + 32 * 512 * 2 + 32 * 32 * 16
+    assert lib.query_absorbed_workspace_size(d, 32, 100, 512) == 0

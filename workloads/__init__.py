@@ -257,3 +257,25 @@ def kv_down_layout(seq_lens: Sequence[int], new_lens: Sequence[int], seed: int):
     for j, (b, k) in enumerate(need):
         table[b, k] = perm[j]
     return np.concatenate(token_seq), np.concatenate(token_pos), table, num_blocks, max_blocks
+
+
+@dataclasses.dataclass
+class QueryInputs:
+    """Inputs of the query path (bf16 bit patterns)."""
+    x: np.ndarray       # [T, dim] hidden states, N(0, 1)
+    w_dq: np.ndarray    # [q_rank, dim] wq_a weight, N(0, 1/dim)
+    gamma_q: np.ndarray # [q_rank] q_norm weight, 1 + N(0, 0.25^2)
+    w_uq: np.ndarray    # [n_heads (128 + 64), q_rank] wq_b weight, N(0, 1/q_rank)
+    w_uk: np.ndarray    # [n_heads, 128, 512] W_UK, N(0, 1/512)
+
+
+def make_query_inputs(seed: int, num_tokens: int, dim: int, n_heads: int, q_rank: int) -> QueryInputs:
+    """Draw order: x -> w_dq -> gamma_q -> w_uq -> w_uk (numpy PCG64). Weight stds 1/sqrt(fan-in) give
+    unit-variance projections; W_UK as in make_case."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal_bf16(rng, (num_tokens, dim))
+    w_dq = _normal_bf16(rng, (q_rank, dim), 1.0 / math.sqrt(dim))
+    gamma_q = bf16_bits(1.0 + 0.25 * rng.standard_normal(q_rank))
+    w_uq = _normal_bf16(rng, (n_heads * (D_NOPE + D_ROPE), q_rank), 1.0 / math.sqrt(q_rank))
+    w_uk = _normal_bf16(rng, (n_heads, D_NOPE, D_C), 1.0 / math.sqrt(D_C))
+    return QueryInputs(x=x, w_dq=w_dq, gamma_q=gamma_q, w_uq=w_uq, w_uk=w_uk)
