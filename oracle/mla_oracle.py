@@ -484,6 +484,13 @@ def combine(o_partial: np.ndarray, lse_partial: np.ndarray, w_uv: np.ndarray):
     Splits with lse = -inf weigh nothing; if all are -inf the output is 0 and lse* = -inf.
     o_partial [B, H, S, d_c] float; lse_partial [B, H, S]; w_uv [H, d_v, d_c] bf16.
     """
+    o_lat, lse = merge_splits(o_partial, lse_partial)
+    out = np.einsum("hvc,bhc->bhv", bf16_to_f64(w_uv), o_lat)
+    return out, lse
+
+
+def merge_splits(o_partial: np.ndarray, lse_partial: np.ndarray):
+    """The log-sum-exp merge of combine() alone: (o_lat [B, H, d_c], lse* [B, H]), float64."""
     o_partial = np.asarray(o_partial, dtype=np.float64)
     lse_partial = np.asarray(lse_partial, dtype=np.float64)
     m = np.max(lse_partial, axis=2, keepdims=True)
@@ -494,8 +501,34 @@ def combine(o_partial: np.ndarray, lse_partial: np.ndarray, w_uv: np.ndarray):
     lse = np.where(finite, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)[..., 0]
     wn = np.where(finite, w / np.where(z > 0, z, 1.0), 0.0)
     o_lat = np.einsum("bhs,bhsc->bhc", wn, np.where(wn[..., None] > 0, o_partial, 0.0))
-    out = np.einsum("hvc,bhc->bhv", bf16_to_f64(w_uv), o_lat)
-    return out, lse
+    return o_lat, lse
+
+
+# ----------------------------------------------------------------------------- output side
+
+def output_projection(out_heads: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """wo applied to the flattened per-head attention output ([P1] section 2: the heads' outputs,
+    [n_heads, v_head_dim] per token, flattened head-major, through wo). out_heads [T, H, d_v],
+    w_o [dim, H d_v] bf16 bits -> y [T, dim] bf16 bits (one rounding of the fp64 product)."""
+    T = out_heads.shape[0]
+    return f64_to_bf16(bf16_to_f64(out_heads).reshape(T, -1) @ bf16_to_f64(w_o).T)
+
+
+def fold_output_weights(w_o: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """W_OV[:, h d_c:(h+1) d_c] = W_O[:, h d_v:(h+1) d_v] W_UV[h]: wo multiplied into each head's value
+    up-projection ahead of time (the value-side counterpart of [P1] section 4's absorption), so the
+    merged latent o_lat[h] feeds the output projection directly. w_o [dim, H d_v], w_uv [H, d_v, d_c]
+    bf16 bits -> [dim, H d_c] bf16 bits (the fp64 product rounded once)."""
+    H, d_v, d_c = np.asarray(w_uv).shape
+    wo = bf16_to_f64(w_o).reshape(-1, H, d_v)
+    return f64_to_bf16(np.einsum("nhv,hvc->nhc", wo, bf16_to_f64(w_uv)).reshape(wo.shape[0], H * d_c))
+
+
+def output_folded(o_lat: np.ndarray, w_ov: np.ndarray) -> np.ndarray:
+    """y = o_lat (flattened head-major) W_OV^T: o_lat [T, H, d_c], w_ov [dim, H d_c] bf16 bits ->
+    y [T, dim] bf16 bits."""
+    T = o_lat.shape[0]
+    return f64_to_bf16(bf16_to_f64(o_lat).reshape(T, -1) @ bf16_to_f64(w_ov).T)
 
 
 # ----------------------------------------------------------------------------- closed forms

@@ -419,10 +419,41 @@ def pin_query_path():
     assert np.array_equal(O.query_absorbed(x, pos, bf16_bits(w_dq), gamma, 1e-6, w_uqk, wr), rows)
 
 
+def pin_output_side():
+    # a wo whose rows pick single (head, value) entries makes the output projection a copy of the
+    # picked attention outputs, and the folded weight a copy of the picked W_UV rows: both routes
+    # then give the same bits for out = bf16(W_UV o_lat)
+    rng = np.random.default_rng(9)
+    H, d_v, d_c, dim, T = 3, 4, 6, 5, 2
+    w_uv = bf16_bits(rng.standard_normal((H, d_v, d_c)))
+    o_lat = bf16_bits(rng.standard_normal((T, H, d_c)))
+    pick = rng.permutation(H * d_v)[:dim]
+    w_o = np.zeros((dim, H * d_v))
+    w_o[np.arange(dim), pick] = 1.0
+    w_o = bf16_bits(w_o)
+    out = O.f64_to_bf16(np.einsum("hvc,thc->thv", O.bf16_to_f64(w_uv), O.bf16_to_f64(o_lat)))
+    y = O.output_projection(out, w_o)
+    assert np.array_equal(y, out.reshape(T, -1)[:, pick])
+    w_ov = O.fold_output_weights(w_o, w_uv)
+    assert w_ov.shape == (dim, H * d_c)
+    for n, p in enumerate(pick):
+        h, v = divmod(int(p), d_v)
+        row = np.zeros((H, d_c), np.uint16)
+        row[h] = w_uv[h, v]
+        assert np.array_equal(w_ov[n], row.reshape(-1))
+    assert np.array_equal(O.output_folded(o_lat, w_ov), y)
+    # the merge that feeds it is combine() without W_UV
+    o_part = rng.standard_normal((T, H, 3, d_c))
+    lse_part = rng.standard_normal((T, H, 3))
+    o_m, l_m = O.merge_splits(o_part, lse_part)
+    o_c, l_c = O.combine(o_part, lse_part, bf16_bits(np.eye(d_c)[None].repeat(H, 0)))
+    assert np.allclose(o_m, o_c, rtol=0, atol=1e-15) and np.array_equal(l_m, l_c)
+
+
 PINS = [pin_bf16_rounding, pin_rope_complex_form, pin_rope_invariants, pin_bruteforce_decode,
         pin_bruteforce_prefill, pin_absorbed_equals_expanded, pin_special_cases, pin_wuk_zero_matches_sdpa,
         pin_split_invariance, pin_prefill_equals_decodes, pin_slot_mapping, pin_closed_forms, pin_rms_norm,
-        pin_kv_down, pin_query_path]
+        pin_kv_down, pin_query_path, pin_output_side]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -515,7 +546,17 @@ def _mut_uqk_transposed(monkeypatch):
         np.einsum("hdc,hdr->hrc", O.bf16_to_f64(wk), O.bf16_to_f64(wn))))
 
 
+def _mut_fold_head_order(monkeypatch):
+    # heads of wo taken value-major instead of head-major
+    def bad(w_o, w_uv):
+        H, d_v, d_c = np.asarray(w_uv).shape
+        wo = O.bf16_to_f64(w_o).reshape(-1, d_v, H).transpose(0, 2, 1)
+        return O.f64_to_bf16(np.einsum("nhv,hvc->nhc", wo, O.bf16_to_f64(w_uv)).reshape(wo.shape[0], H * d_c))
+    monkeypatch.setattr(O, "fold_output_weights", bad)
+
+
 MUTANTS = [
+    (_mut_fold_head_order, [pin_output_side]),
     (_mut_q_split_swapped, [pin_query_path]),
     (_mut_uqk_transposed, [pin_query_path]),
     (_mut_rms_sum, [pin_rms_norm]),
