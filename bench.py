@@ -45,14 +45,15 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "prefill", "prefill_crossover", "kv_down", "query"],
+    ap.add_argument("--workload", choices=["decode", "prefill", "prefill_crossover", "kv_down", "query", "output"],
                     default="decode",
                     help="decode: B=32, n_h=128, 4K context (the headline); prefill: chunked prefill, 2 x 1024 "
                          "new tokens after 8192 cached; prefill_crossover: absorbed against expanded prefill over "
                          "chunk lengths 64..2048 after 8192 cached; kv_down: KV down-projection + kv_norm + RoPE "
                          "append of the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096; "
                          "query: the absorbed query rows of the decode step's 32 tokens straight from the hidden "
-                         "state (W_UQ W_UK multiplied ahead of time), width 4096, rank 512")
+                         "state (W_UQ W_UK multiplied ahead of time), width 4096, rank 512; output: the decode "
+                         "step's output side, W_UV folded into wo against combine + wo, 32 tokens, width 4096")
     return ap.parse_args()
 
 
@@ -167,6 +168,8 @@ def main():
         return crossover_main(args, torch, lib, props)
     if args.workload == "query":
         return query_main(args, torch, lib, props)
+    if args.workload == "output":
+        return output_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -464,6 +467,93 @@ def crossover_main(args, torch, lib, props):
 KV_DIM = 4096
 KV_EPS = 1e-6
 Q_RANK = 512
+
+
+def output_main(args, torch, lib, props):
+    """The decode step's output side from the attention's split partials (32 rows, 128 heads, 8 splits):
+    folded = mla_decode_merge_latent + mla_output_projection with W_OV = W_O W_UV per head;
+    unfolded = mla_decode_combine (W_UV) + mla_output_projection with W_O."""
+    from workloads import make_output_inputs
+    T, H, S, dim = 32, 128, 8, KV_DIM
+    dims = lib.make_dims(H)
+    rng = np.random.default_rng(7)
+    sets = []
+    for k in range(2):  # 2 x 0.7 GB of weights
+        inp = make_output_inputs(600 + k, T, dim, H)
+        st = {"w_o": torch.from_numpy(inp.w_o.view(np.int16)).cuda(), "w_uv": torch.from_numpy(inp.w_uv.view(np.int16)).cuda()}
+        st["o_part"] = torch.from_numpy(rng.standard_normal((T, H, S, 512)).astype(np.float32)).cuda().to(torch.bfloat16)
+        st["lse_part"] = torch.from_numpy(rng.standard_normal((T, H, S)).astype(np.float32)).cuda()
+        st["w_op"] = torch.empty(dim * H * 128, dtype=torch.int16, device="cuda")
+        st["w_ov"] = torch.empty(dim * H * 512, dtype=torch.int16, device="cuda")
+        lib.prepare_output_weight(dims, st["w_o"], st["w_op"])
+        lib.fold_output_weights(dims, st["w_o"], st["w_uv"], st["w_ov"])
+        st["o_lat"] = torch.empty((T, H, 512), dtype=torch.int16, device="cuda")
+        st["out"] = torch.empty((T, H, 128), dtype=torch.int16, device="cuda")
+        st["lse"] = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        st["y"] = torch.empty((T, dim), dtype=torch.int16, device="cuda")
+        st["ws_f"] = torch.empty(lib.output_projection_workspace_size(dims, T, dim, True), dtype=torch.uint8, device="cuda")
+        st["ws_u"] = torch.empty(lib.output_projection_workspace_size(dims, T, dim, False), dtype=torch.uint8,
+                                 device="cuda")
+        sets.append(st)
+    torch.cuda.synchronize()
+    n = len(sets)
+    fns = {
+        "merge_latent": lambda i: lib.decode_merge_latent(dims, T, S, sets[i % n]["o_part"], sets[i % n]["lse_part"],
+                                                          sets[i % n]["o_lat"], sets[i % n]["lse"]),
+        "folded_projection": lambda i: lib.output_projection(dims, sets[i % n]["o_lat"], sets[i % n]["w_ov"], dim, True,
+                                                             sets[i % n]["ws_f"], sets[i % n]["y"]),
+        "combine_wuv": lambda i: lib.decode_combine(dims, T, S, sets[i % n]["o_part"], sets[i % n]["lse_part"],
+                                                    sets[i % n]["w_uv"], sets[i % n]["out"], sets[i % n]["lse"]),
+        "wo_projection": lambda i: lib.output_projection(dims, sets[i % n]["out"], sets[i % n]["w_op"], dim, False,
+                                                         sets[i % n]["ws_u"], sets[i % n]["y"]),
+    }
+    ms = {}
+    for name, fn in fns.items():
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ms[name] = time_each(torch, fn, args.steps)
+    ms_fold = ms["merge_latent"] + ms["folded_projection"]
+    ms_unf = ms["combine_wuv"] + ms["wo_projection"]
+    fbytes = dim * H * 512 * 2 + T * H * 512 * 2 + T * dim * 2
+    gbps = fbytes / (ms["folded_projection"] * 1e-3) / 1e9
+    result = {
+        "metric": "folded output projection (W_O W_UV per head) GB/s, 32 decode rows, width 4096",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms["folded_projection"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"mla_output_projection folded T={T} n_h={H} dim={dim} (after an {S}-split decode)",
+                   "num_tokens": T, "n_heads": H, "dim": dim, "splits": S, "input_sets_rotated": n},
+        "roofline": {"kernel": "mla_output_projection folded (oo_splitk_gemm_kernel + reduce_bf16_kernel)",
+                     "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes_per_launch": fbytes},
+        "kernels_ms": {k: round(v, 5) for k, v in ms.items()},
+        "routes_ms": {"folded: merge + W_OV projection": round(ms_fold, 5),
+                      "unfolded: combine with W_UV + wo projection": round(ms_unf, 5)},
+        "weight_bytes": {"folded_W_OV": dim * H * 512 * 2, "unfolded_W_UV_and_W_O": H * 128 * 512 * 2 + dim * H * 128 * 2},
+        "device": props.name,
+    }
+    if not args.no_cpu:
+        from oracle import mla_oracle as O
+        inp = make_output_inputs(600, T, dim, H)
+        rows = np.arange(64)
+        w_ov = O.fold_output_weights(inp.w_o[rows], inp.w_uv)
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            O.output_folded(inp.o_lat, w_ov)
+            reps += 1
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        sample_bytes = 64 * H * 512 * 2 + T * H * 512 * 2 + T * 64 * 2
+        result["cpu_baseline"] = {"value": round(reps * sample_bytes / dt / 1e9, 4), "unit": "GB/s",
+                                  "cores": int(threads), "kind": "oracle",
+                                  "sample": f"{reps} repetitions of the folded projection onto 64 of the {dim} "
+                                            f"output columns (the weight folded outside the timing), fp64, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
 
 
 def query_bytes(T, H, dim, r):

@@ -84,6 +84,63 @@ int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_to
                                           q_rope_inout, dims->rope_theta, stream));
 }
 
+int mla_decode_merge_latent(const mla_dims* dims, int32_t batch, int32_t num_splits, const uint16_t* o_partial,
+                            const float* lse_partial, uint16_t* o_lat, float* lse_out, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || num_splits < 1) return MLA_ERR_BAD_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!o_partial || !lse_partial || !o_lat) return MLA_ERR_NULL;
+  if (((uintptr_t)o_partial & 15) != 0 || ((uintptr_t)o_lat & 15) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_merge_latent(batch, dims->n_heads, num_splits, o_partial, lse_partial, o_lat, lse_out,
+                                           stream));
+}
+
+int mla_prepare_output_weight(const mla_dims* dims, int32_t dim, const uint16_t* w_o, uint16_t* w_o_prepared,
+                              hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dim <= 0) return MLA_ERR_BAD_ARG;
+  if (dim % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!w_o || !w_o_prepared) return MLA_ERR_NULL;
+  if (((uintptr_t)w_o & 15) != 0 || ((uintptr_t)w_o_prepared & 15) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_prepare_rows(dim, (int64_t)dims->n_heads * dims->d_v, w_o, w_o_prepared, stream));
+}
+
+int mla_fold_output_weights(const mla_dims* dims, int32_t dim, const uint16_t* w_o, const uint16_t* w_uv,
+                            uint16_t* w_ov_prepared, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dim <= 0) return MLA_ERR_BAD_ARG;
+  if (dim % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!w_o || !w_uv || !w_ov_prepared) return MLA_ERR_NULL;
+  if (((uintptr_t)w_ov_prepared & 7) != 0) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_fold_output_weights(dim, dims->n_heads, w_o, w_uv, w_ov_prepared, stream));
+}
+
+size_t mla_output_projection_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim, int32_t folded) {
+  if (check_dims(dims) != MLA_OK || num_tokens < 0 || dim <= 0 || dim % 64 != 0) return 0;
+  const int64_t K = (int64_t)dims->n_heads * (folded ? dims->d_c : dims->d_v);
+  return mla::output_workspace_bytes(num_tokens, dim, K);
+}
+
+int mla_output_projection(const mla_dims* dims, int32_t num_tokens, int32_t dim, int32_t folded, const uint16_t* act,
+                          const uint16_t* w_prepared, void* workspace, size_t workspace_bytes, uint16_t* y,
+                          hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535 * 32 || dim <= 0) return MLA_ERR_BAD_ARG;
+  if (dim % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MLA_OK;
+  if (!act || !w_prepared || !workspace || !y) return MLA_ERR_NULL;
+  const int64_t K = (int64_t)dims->n_heads * (folded ? dims->d_c : dims->d_v);
+  if (workspace_bytes < mla::output_workspace_bytes(num_tokens, dim, K)) return MLA_ERR_BAD_ARG;
+  if (((uintptr_t)workspace & 255) != 0 || ((uintptr_t)act & 15) != 0 || ((uintptr_t)w_prepared & 15) != 0 ||
+      ((uintptr_t)y & 7) != 0)
+    return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_output_gemm(num_tokens, dim, K, act, w_prepared, workspace, y, stream));
+}
+
 int mla_absorb_query_weights(const mla_dims* dims, int32_t q_rank, const uint16_t* w_uq, const uint16_t* w_uk,
                              uint16_t* w_q, hipStream_t stream) {
   int st = check_dims(dims);

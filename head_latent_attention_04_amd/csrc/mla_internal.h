@@ -123,6 +123,19 @@ hipError_t launch_query_absorbed(int n_heads, int num_tokens, const int32_t* tok
                                  const uint16_t* w_q, float theta, void* workspace, uint16_t* q_abs,
                                  hipStream_t stream);
 
+// Output side. merge: the split partials of mla_decode_attend merged into the normalised latent
+// o_lat [rows, n_heads, 512] bf16 (no W_UV). Weights in MFMA operand order (prepare_rows: any
+// row-major [N, K]; fold: W_OV = W_O W_UV per head, [dim, n_heads 512]). output_gemm: y [M, N] bf16
+// = act [M, K] times the prepared weight's rows, split over K (workspace: fp32 partials).
+hipError_t launch_merge_latent(int rows, int n_heads, int num_splits, const uint16_t* o_partial,
+                               const float* lse_partial, uint16_t* o_lat, float* lse_out, hipStream_t stream);
+hipError_t launch_prepare_rows(int N, int64_t K, const uint16_t* w, uint16_t* w_op, hipStream_t stream);
+hipError_t launch_fold_output_weights(int dim, int n_heads, const uint16_t* w_o, const uint16_t* w_uv,
+                                      uint16_t* w_ov, hipStream_t stream);
+size_t output_workspace_bytes(int M, int N, int64_t K);
+hipError_t launch_output_gemm(int M, int N, int64_t K, const uint16_t* act, const uint16_t* w_op, void* workspace,
+                              uint16_t* y, hipStream_t stream);
+
 // Expanded-form chunked prefill: up-projected keys and values ([batch, n_heads, lpad, 128] each,
 // lpad = max_seq_len rounded up to 128, in the workspace), then causal attention with 192-wide keys.
 size_t prefill_expanded_kv_bytes(int batch, int n_heads, int max_seq_len);

@@ -44,6 +44,11 @@ EXPORTS = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_rope_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp,
                                        _vp, _vp]),
+    "mla_decode_merge_latent": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "mla_prepare_output_weight": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp]),
+    "mla_fold_output_weights": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp, _vp]),
+    "mla_output_projection_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32, _i32]),
+    "mla_output_projection": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]),
     "mla_absorb_query_weights": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp, _vp]),
     "mla_query_absorbed_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32, _i32]),
     "mla_query_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
@@ -149,6 +154,48 @@ def rope_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_ro
         _ptr(k_rope, "k_rope", BF16, T * dims.d_rope),
         _ptr(q_rope, "q_rope", BF16, T * dims.n_heads * dims.d_rope), _stream(stream))
     _check("mla_rope_append", st)
+
+
+def decode_merge_latent(dims: MlaDims, batch: int, num_splits: int, o_partial, lse_partial, o_lat, lse_out=None,
+                        stream=None):
+    H = dims.n_heads
+    st = load().mla_decode_merge_latent(
+        ctypes.byref(dims), batch, num_splits, _ptr(o_partial, "o_partial", BF16, batch * H * num_splits * dims.d_c),
+        _ptr(lse_partial, "lse_partial", F32, batch * H * num_splits), _ptr(o_lat, "o_lat", BF16, batch * H * dims.d_c),
+        _ptr(lse_out, "lse_out", F32, batch * H), _stream(stream))
+    _check("mla_decode_merge_latent", st)
+
+
+def prepare_output_weight(dims: MlaDims, w_o, w_o_prepared, stream=None):
+    dim = w_o.shape[0]
+    K = dims.n_heads * dims.d_v
+    st = load().mla_prepare_output_weight(ctypes.byref(dims), dim, _ptr(w_o, "w_o", BF16, dim * K),
+                                          _ptr(w_o_prepared, "w_o_prepared", BF16, dim * K), _stream(stream))
+    _check("mla_prepare_output_weight", st)
+
+
+def fold_output_weights(dims: MlaDims, w_o, w_uv, w_ov, stream=None):
+    dim = w_o.shape[0]
+    H = dims.n_heads
+    st = load().mla_fold_output_weights(
+        ctypes.byref(dims), dim, _ptr(w_o, "w_o", BF16, dim * H * dims.d_v),
+        _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c), _ptr(w_ov, "w_ov", BF16, dim * H * dims.d_c),
+        _stream(stream))
+    _check("mla_fold_output_weights", st)
+
+
+def output_projection_workspace_size(dims: MlaDims, num_tokens: int, dim: int, folded: bool) -> int:
+    return int(load().mla_output_projection_workspace_size(ctypes.byref(dims), num_tokens, dim, int(folded)))
+
+
+def output_projection(dims: MlaDims, act, w_prepared, dim: int, folded: bool, workspace, y, stream=None):
+    T = act.shape[0]
+    K = dims.n_heads * (dims.d_c if folded else dims.d_v)
+    st = load().mla_output_projection(
+        ctypes.byref(dims), T, dim, int(folded), _ptr(act, "act", BF16, T * K),
+        _ptr(w_prepared, "w_prepared", BF16, dim * K), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(y, "y", BF16, T * dim), _stream(stream))
+    _check("mla_output_projection", st)
 
 
 def absorb_query_weights(dims: MlaDims, w_uq, w_uk, w_q, stream=None):

@@ -244,6 +244,40 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
                         size_t workspace_bytes, uint16_t* out, float* lse_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * The output side ("论文复现工坊 No.4", section 2: the heads' outputs [n_heads, d_v] flattened
+ * head-major and projected by wo; section 4's absorption taken on the value side: W_UV folded into
+ * wo, so decode hands the merged latent straight to the output GEMM).
+ *
+ * mla_decode_merge_latent - the log-sum-exp merge of mla_decode_combine without W_UV:
+ *   o_lat[b, h] = sum_s exp(lse_s - lse*) o_partial[b, h, s] / sum_s exp(lse_s - lse*)  (bf16, 512 wide),
+ *   lse_out[b, h] = lse* (or NULL); a row whose splits are all empty gives zeros and -inf.
+ *   o_partial, lse_partial as written by mla_decode_attend; o_lat [batch, n_heads, 512] bf16;
+ *   o_partial and o_lat 16-byte aligned.
+ * mla_prepare_output_weight - wo's weight W_O [dim, n_heads d_v] (row-major, bf16) copied into MFMA
+ *   operand order: row n, element k at (((n / 32) (K / 16) + k / 16) 64 + n % 32 + 32 ((k / 8) % 2)) 8
+ *   + k % 8 with K = n_heads d_v (16-byte aligned buffers).
+ * mla_fold_output_weights - W_OV[:, h d_c:(h+1) d_c] = W_O[:, h d_v:(h+1) d_v] W_UV[h] (fp32 sums, one
+ *   rounding), [dim, n_heads d_c] in the same operand order with K = n_heads d_c (w_ov 8-byte aligned).
+ * mla_output_projection - y [num_tokens, dim] bf16 = act W^T, W the prepared weight:
+ *   folded = 0: act = the attention output [num_tokens, n_heads, d_v] (mla_decode_combine's out),
+ *               W = mla_prepare_output_weight's;  y = wo(out)
+ *   folded = 1: act = o_lat [num_tokens, n_heads, d_c] (mla_decode_merge_latent's), W = W_OV
+ *   fp32 partial sums over splits of K in the workspace (>= mla_output_projection_workspace_size
+ *   bytes, 256-byte aligned), one rounding; act and W 16-byte aligned, y 8-byte aligned.
+ * dim must be a positive multiple of 64 (else MLA_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------------------------- */
+int mla_decode_merge_latent(const mla_dims* dims, int32_t batch, int32_t num_splits, const uint16_t* o_partial,
+                            const float* lse_partial, uint16_t* o_lat, float* lse_out, hipStream_t stream);
+int mla_prepare_output_weight(const mla_dims* dims, int32_t dim, const uint16_t* w_o, uint16_t* w_o_prepared,
+                              hipStream_t stream);
+int mla_fold_output_weights(const mla_dims* dims, int32_t dim, const uint16_t* w_o, const uint16_t* w_uv,
+                            uint16_t* w_ov_prepared, hipStream_t stream);
+size_t mla_output_projection_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim, int32_t folded);
+int mla_output_projection(const mla_dims* dims, int32_t num_tokens, int32_t dim, int32_t folded, const uint16_t* act,
+                          const uint16_t* w_prepared, void* workspace, size_t workspace_bytes, uint16_t* y,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * The query path with the query and key projections multiplied ahead of time
  * ("论文复现工坊 No.4", section 2: wq_a, q_norm (RMSNorm over q_lora_rank), wq_b with per-head
  * output [q_nope (d_nope) | q_R (d_rope)]; section 4: the absorbed query is scored against c_KV;

@@ -279,3 +279,22 @@ def make_query_inputs(seed: int, num_tokens: int, dim: int, n_heads: int, q_rank
     w_uq = _normal_bf16(rng, (n_heads * (D_NOPE + D_ROPE), q_rank), 1.0 / math.sqrt(q_rank))
     w_uk = _normal_bf16(rng, (n_heads, D_NOPE, D_C), 1.0 / math.sqrt(D_C))
     return QueryInputs(x=x, w_dq=w_dq, gamma_q=gamma_q, w_uq=w_uq, w_uk=w_uk)
+
+
+@dataclasses.dataclass
+class OutputInputs:
+    """Inputs of the output side (bf16 bit patterns)."""
+    out: np.ndarray     # [T, n_heads, 128] per-head attention outputs, N(0, 1)
+    o_lat: np.ndarray   # [T, n_heads, 512] merged latents, N(0, 1)
+    w_o: np.ndarray     # [dim, n_heads 128] wo weight, N(0, 1/(n_heads 128))
+    w_uv: np.ndarray    # [n_heads, 128, 512] W_UV, N(0, 1/512)
+
+
+def make_output_inputs(seed: int, num_tokens: int, dim: int, n_heads: int) -> OutputInputs:
+    """Draw order: out -> o_lat -> w_o -> w_uv (numpy PCG64); fan-in stds as elsewhere."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = _normal_bf16(rng, (num_tokens, n_heads, D_V))
+    o_lat = _normal_bf16(rng, (num_tokens, n_heads, D_C))
+    w_o = _normal_bf16(rng, (dim, n_heads * D_V), 1.0 / math.sqrt(n_heads * D_V))
+    w_uv = _normal_bf16(rng, (n_heads, D_V, D_C), 1.0 / math.sqrt(D_C))
+    return OutputInputs(out=out, o_lat=o_lat, w_o=w_o, w_uv=w_uv)
