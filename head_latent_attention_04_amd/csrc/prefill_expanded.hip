@@ -32,6 +32,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kXcds = 8;
@@ -130,13 +132,16 @@ constexpr int kUpTok = 256, kUpW = 256, kUpWaves = 8, kUpStages = 2;
 constexpr int kUpStageBytes = (kUpTok + kUpW) * kSeg;  // 64 KB
 constexpr int kUpInstr = 8;                              // copy instructions per wave per stage
 constexpr int kUpPad = 128;                              // lpad granule
+constexpr int kUpOutPitch = 2 * kDnope * 2 + 16;         // staged output row: keys | values, padded (528 B)
+constexpr int kUpLds = kUpStages * kUpStageBytes > kUpTok * kUpOutPitch ? kUpStages * kUpStageBytes
+                                                                        : kUpTok * kUpOutPitch;
 
 __global__ void __launch_bounds__(512) upproj_kernel(CacheView cache, const int32_t* __restrict__ seq_lens,
                                                      int n_heads, int mtiles, int lpad,
                                                      const uint16_t* __restrict__ w_uk,
                                                      const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ k_up,
                                                      uint16_t* __restrict__ v_up) {
-  __shared__ __attribute__((aligned(1024))) char smem[kUpStages * kUpStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kUpLds];
   lds_char* lds = (lds_char*)smem;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
@@ -213,24 +218,36 @@ __global__ void __launch_bounds__(512) upproj_kernel(CacheView cache, const int3
     });
   }
 
-  // D layout: lane holds token column lane % 32 and weight rows 8 (e / 4) + 4 (lane / 32) + e % 4 of
-  // a block: four consecutive output elements per (block, e / 4), stored as 8 bytes. Rows past lpad
-  // (a last tile that overhangs it) are not stored.
-  uint16_t* dst = (wn == 0 ? k_up : v_up) + ((int64_t)(b * n_heads + h) * lpad) * kDnope;
+  // The tile goes out through LDS as whole rows: staged as [token][keys (256 B) | values (256 B)] with
+  // a padded pitch, then every store instruction writes two tokens' 512 bytes (two 256-byte rows of
+  // K_up and of V_up). D layout: lane holds token column lane % 32 and weight rows
+  // 8 (e / 4) + 4 (lane / 32) + e % 4 of a block, i.e. four consecutive outputs per (block, e / 4).
+  wg_barrier();  // every wave is done reading the stages
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int t = m0 + 64 * wm + 32 * i + (lane & 31);
-    if (t >= lpad) continue;
-    uint16_t* drow = dst + (int64_t)t * kDnope;
+    const int tl = 64 * wm + 32 * i + (lane & 31);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int d = 32 * j + 8 * e4 + 4 * khalf;
-        const uint2 v = make_uint2(pack_bf16x4_lo(acc[j][i][4 * e4], acc[j][i][4 * e4 + 1]),
-                                   pack_bf16x4_lo(acc[j][i][4 * e4 + 2], acc[j][i][4 * e4 + 3]));
-        *reinterpret_cast<uint2*>(drow + d) = v;
+        const int col = 128 * wn + 32 * j + 8 * e4 + 4 * khalf;
+        const u32x2 v = {pack_bf16x4_lo(acc[j][i][4 * e4], acc[j][i][4 * e4 + 1]),
+                         pack_bf16x4_lo(acc[j][i][4 * e4 + 2], acc[j][i][4 * e4 + 3])};
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + tl * kUpOutPitch + 2 * col) = v;
       }
+  }
+  wg_barrier();
+  const int64_t kvbase = ((int64_t)(b * n_heads + h) * lpad + m0) * kDnope;
+  // 256 tokens x 32 chunks of 16 bytes; thread t takes chunk t % 32 of tokens t / 32 + 16 k. Rows past
+  // lpad (a last tile that overhangs it) are not stored.
+  const int c = threadIdx.x & 31, part = c >> 4, cc = c & 15;
+  uint16_t* dst = (part == 0 ? k_up : v_up) + kvbase + 8 * cc;
+#pragma unroll 4
+  for (int k = 0; k < kUpTok / 16; ++k) {
+    const int tl = (threadIdx.x >> 5) + 16 * k;
+    if (m0 + tl >= lpad) break;
+    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + tl * kUpOutPitch + 16 * c);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)tl * kDnope) = v;
   }
 }
 
