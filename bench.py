@@ -719,7 +719,7 @@ def kv_down_main(args, torch, lib, props):
                                f"bf16 latent cache", "num_tokens": T_dec, "dim": KV_DIM, "d_c": 512, "d_rope": 64,
                    "input_sets_rotated": len(dec)},
         "ms_back_to_back": {k: round(v["back_to_back"], 5) for k, v in res.items()},
-        "roofline": {"kernel": "mla_kv_down_append (kv_down_gemm_kernel + kv_down_finish_kernel)", "bound": "hbm",
+        "roofline": {"kernel": "mla_kv_down_append (splitk_gemm_kernel + kv_down_finish_kernel)", "bound": "hbm",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": kv_down_bytes(T_dec)},

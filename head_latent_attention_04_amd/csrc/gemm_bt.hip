@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) gemm_bt_partial_kernel(int M, int N, int 
 // K steps of operands in flight; the four partial tiles are added through LDS. Many splits spread
 // the weight B over many work-groups, so it streams from HBM once at full width.
 constexpr int kKStep = 16;  // K per MFMA
-constexpr int kAhead = 2;   // K steps whose operands are loaded ahead
+constexpr int kAhead = 4;   // K steps whose operands are loaded ahead (a 64-long quarter at once)
 
 __global__ void __launch_bounds__(256) splitk_gemm_kernel(int M, int N, int K, int split_len,
                                                           const uint16_t* __restrict__ A,

@@ -57,13 +57,21 @@ __global__ void __launch_bounds__(256) kv_down_finish_kernel(CacheView cache, in
   // pairs each). All split partials are loaded before the first add (one memory latency), then
   // added in split order.
   const bool live = tid < kRowOut / 4;
+  const int seq = token_seq[i], pos = token_pos[i];
   const float4* p4 = reinterpret_cast<const float4*>(part) + (int64_t)i * (kRowOut / 4) + tid;
   const int64_t split_stride = (int64_t)num_tokens * (kRowOut / 4);
   float4 v[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
     v[s] = (live && s < nsplit) ? p4[s * split_stride] : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int seq = token_seq[i], pos = token_pos[i];
+  // the RoPE threads take their angles (fp64) while the partials are on their way
+  const bool rope_thread = live && tid >= kDc / 4;
+  const int j = 2 * (tid - kDc / 4);
+  double rc[2] = {1.0, 1.0}, rs[2] = {0.0, 0.0};
+  if (rope_thread) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) rope_cos_sin(pos, j + e, log2_theta, &rc[e], &rs[e]);
+  }
   float kv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
@@ -95,15 +103,10 @@ __global__ void __launch_bounds__(256) kv_down_finish_kernel(CacheView cache, in
         make_uint2((uint32_t)c[0] | ((uint32_t)c[1] << 16), (uint32_t)c[2] | ((uint32_t)c[3] << 16));
   } else {
     // k_R (rounded to bf16 above) turned by the token's position, pairs j and j + 1
-    const int j = 2 * (tid - kDc / 4);
     uint32_t w[2] = {(uint32_t)f32_to_bf16(kv[0]) | ((uint32_t)f32_to_bf16(kv[1]) << 16),
                      (uint32_t)f32_to_bf16(kv[2]) | ((uint32_t)f32_to_bf16(kv[3]) << 16)};
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      double c, sn;
-      rope_cos_sin(pos, j + e, log2_theta, &c, &sn);
-      w[e] = rope_turn_pair(w[e], c, sn);
-    }
+    for (int e = 0; e < 2; ++e) w[e] = rope_turn_pair(w[e], rc[e], rs[e]);
     reinterpret_cast<uint2*>(row + kDc)[tid - kDc / 4] = make_uint2(w[0], w[1]);
   }
 }
