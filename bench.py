@@ -105,6 +105,20 @@ def time_each(torch, fn, n):
     return sum(a.elapsed_time(b) for a, b in ev) / n
 
 
+def time_percentiles(torch, fn, n):
+    """p10, p50 and p90 (ms) of n calls, each bracketed by its own pair of events on the launch
+    stream (the calls still run back to back)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(s)
+        fn(i)
+        ev[i][1].record(s)
+    ev[-1][1].synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return [round(t[min(n - 1, int(q * n))], 5) for q in (0.1, 0.5, 0.9)]
+
+
 def cpu_baseline(case, budget_s):
     """fp64 expanded-form oracle on whole sequences (all heads) of the same workload, until the
     time budget is spent; rate in the metric's unit (algorithmic TFLOP/s of absorbed decode)."""
@@ -234,6 +248,10 @@ def main():
         graphs[i % nsets].replay()
     ms_step_graph = time_loop(torch, lambda i: graphs[i % nsets].replay(), args.steps)
     ms_step = ms_step_eager
+    # spread of single steps (rotating input sets, so the cache comes from HBM), and the warm step:
+    # one input set over and over, its weights and part of its cache left in the Infinity Cache
+    step_pct = time_percentiles(torch, step, 100)
+    ms_step_warm = time_loop(torch, lambda i: step(0), args.steps)
 
     # each kernel of the step alone: N launches back to back on the launch stream between one pair of
     # events, rotating the input sets (the absorbed queries of every set are in place); the average
@@ -276,6 +294,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "ms_per_step_graph_replay": round(ms_step_graph, 5),
+        "ms_per_step_p10_p50_p90": step_pct,
+        "ms_per_step_warm_one_input_set": round(ms_step_warm, 5),
         "host_enqueue_us_per_step": round(host["us_per_call"], 1),
         "higher_is_better": True,
         "scaling": "weak",
