@@ -45,9 +45,12 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "prefill", "prefill_crossover", "kv_down", "query", "output"],
+    ap.add_argument("--workload", choices=["decode", "decode_configs", "prefill", "prefill_crossover", "kv_down", "query",
+                                           "output"],
                     default="decode",
-                    help="decode: B=32, n_h=128, 4K context (the headline); prefill: chunked prefill, 2 x 1024 "
+                    help="decode: B=32, n_h=128, 4K context (the headline); decode_configs: the same decode step "
+                         "on the ragged paged batch (B=64, lengths 512..32768) and on the long context (B=4, "
+                         "131072 tokens); prefill: chunked prefill, 2 x 1024 "
                          "new tokens after 8192 cached; prefill_crossover: absorbed against expanded prefill over "
                          "chunk lengths 64..2048 after 8192 cached; kv_down: KV down-projection + kv_norm + RoPE "
                          "append of the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096; "
@@ -176,6 +179,8 @@ def main():
     props = torch.cuda.get_device_properties(0)
     if args.workload == "prefill":
         return prefill_main(args, torch, lib, props)
+    if args.workload == "decode_configs":
+        return decode_configs_main(args, torch, lib, props)
     if args.workload == "kv_down":
         return kv_down_main(args, torch, lib, props)
     if args.workload == "prefill_crossover":
@@ -372,6 +377,73 @@ def prefill_cpu_baseline(case, budget_s):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(rows)} of {len(pos_all)} query tokens (every 97th, all {H} heads), fp64 expanded "
                       f"form, {dt:.1f} s"}
+
+
+def decode_configs_main(args, torch, lib, props):
+    """The decode step (fused RoPE + absorption, split-KV attention, combine with W_UV) on the two
+    other decode workloads: the ragged paged batch (B=64, lengths uniform in [512, 32768], 64-token
+    blocks, shuffled table) and the long context (B=4, 131072 tokens, many splits). One input set
+    each: either cache (1.2 GB, 0.6 GB) is several times the Infinity Cache, so every step reads it
+    from HBM. Roofline per config: the attention kernel's cache bytes against the HBM peak."""
+    from head_latent_attention_04_amd.runner import DeviceCase
+    from workloads import make_config
+
+    out = {}
+    for cfg, label in ((2, "ragged paged B=64, L~U[512,32768]"), (3, "long context B=4, L=131072")):
+        case = make_config(cfg)
+        B, H = case.batch, case.n_heads
+        st, ns = lib.decode_plan(lib.make_dims(H), B, int(case.seq_lens.max()), props.multi_processor_count)
+        ds = DeviceCase(case)
+        ds.fill_history()
+        ds.prepare_step_inputs()
+        ds.alloc_decode(ns)
+        ds.append_new()
+        torch.cuda.synchronize()
+        o_part, lse_part = ds.partials
+
+        def attend(i):
+            lib.decode_attend(ds.dims, ds.cache, ds.seq_lens, ds._ws, st, ns, o_part, lse_part)
+
+        def comb(i):
+            lib.decode_combine(ds.dims, B, ns, o_part, lse_part, ds.w_uv, ds.out, ds.lse)
+
+        def step(i):
+            ds.append_absorb_new(reset_q=False)
+            attend(i)
+            comb(i)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        ms_step = time_loop(torch, step, args.steps)
+        ms_attn = time_loop(torch, attend, args.steps)
+        ms_comb = time_loop(torch, comb, args.steps)
+        tokens = int(case.seq_lens.sum())
+        cache_bytes = tokens * 1152
+        flops = sum(step_flops_one_seq(case, b) for b in range(B))
+        work_groups = sum((int(L) + st - 1) // st for L in case.seq_lens)  # non-empty splits
+        out[f"config{cfg}"] = {
+            "workload": label, "batch": B, "cached_tokens": tokens, "split_tokens": st, "num_splits": ns,
+            "attention_work_groups": work_groups, "ms_per_step": round(ms_step, 5),
+            "step_TFLOPs": round(flops / (ms_step * 1e-3) / 1e12, 1),
+            "latent_kv_GBps_step": round(cache_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "kernels_ms": {"decode_attention": round(ms_attn, 5), "combine_wuv": round(ms_comb, 5)},
+            "roofline": {"kernel": "decode_mfma_kernel<4, true>", "bound": "hbm",
+                         "achieved": round(cache_bytes / (ms_attn * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(cache_bytes / (ms_attn * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "algorithmic_bytes_per_launch": cache_bytes},
+        }
+        del ds, o_part, lse_part
+        torch.cuda.empty_cache()
+    line = {
+        "metric": "absorbed MLA decode latent-KV GB/s on the ragged paged and long-context decode workloads",
+        "value": out["config2"]["latent_kv_GBps_step"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode step on configs 2 (value) and 3", "n_heads": 128, "d_c": 512, "d_rope": 64},
+        **out, "device": props.name,
+    }
+    print(json.dumps(line))
 
 
 def prefill_main(args, torch, lib, props):
