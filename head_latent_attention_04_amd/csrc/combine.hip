@@ -34,7 +34,11 @@ constexpr int kPitch = kDc * 2 + 16;  // bf16 row of 512 latent columns, padded 
 // kChunk: splits whose partials are loaded together (1, 2, 4 or 8: the split count rounded up to a
 // power of two, at most 8). With kChunk <= 2 the next block's partials are loaded while the current
 // block is merged and projected, which matters when a work-group runs many blocks (prefill, S = 1).
-template <int kChunk>
+// kGroups (1 or 4): thread groups that share one sequence's splits. With 4 (small batches with many
+// splits: at most 4 sequences, each row slot of the block holds a quarter of a sequence's splits,
+// s = g, g + 4, ...), the four partial merges meet in LDS, so a sequence's 64 splits take two load
+// round trips instead of eight.
+template <int kChunk, int kGroups>
 __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_heads, int num_splits, int blocks_per_wg,
                                                            const uint16_t* __restrict__ o_partial,
                                                            const float* __restrict__ lse_partial,
@@ -42,30 +46,46 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
                                                            uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   __shared__ __attribute__((aligned(16))) char hi_lds[kRowsPerWg * kPitch];
   __shared__ __attribute__((aligned(16))) char lo_lds[kRowsPerWg * kPitch];
+  __shared__ float red_lds[kGroups > 1 ? kRowsPerWg * kDc : 1];  // per row slot: unnormalised sums
+  __shared__ float stat_lds[2 * kRowsPerWg];                       // per row slot: max, sum of weights
+  constexpr int kRows = kRowsPerWg / kGroups;                      // sequences per block
   const int h = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  const int nblk = (batch + kRowsPerWg - 1) / kRowsPerWg;
+  const int nblk = (batch + kRows - 1) / kRows;
   const int blk_begin = blockIdx.y * blocks_per_wg;
   const int blk_end = min(nblk, blk_begin + blocks_per_wg);
   if (blk_begin >= blk_end) return;
 
-  // Merge role: thread t owns sequence b0 + t / 16 and latent columns 32 (t % 16) .. +31 of a block.
-  const int bl = tid >> 4;
+  // Merge role: thread t owns row slot t / 16 and latent columns 32 (t % 16) .. +31 of a block; the
+  // slot is sequence b0 + slot / kGroups, split group slot % kGroups, whose splits are g, g + kGroups, ...
+  const int slot = tid >> 4;
+  const int bl = slot / kGroups, grp = slot % kGroups;
   const int c0 = 32 * (tid & 15);
+  const int n_my = num_splits > grp ? (num_splits - grp + kGroups - 1) / kGroups : 0;  // this group's splits
+  auto sidx = [&](int j) { return grp + kGroups * j; };
   // The first kChunk splits of a block: log-sum-exps and partials issued together, without branches
   // (an index past the last split reads the last one and gets weight zero).
   constexpr bool kPrefetch = kChunk <= 2;
   float ls[kChunk], ls_next[kChunk];
   uint4 v[kChunk][4], v_next[kChunk][4];
   auto load_first_chunk = [&](int blk, float (&ls)[kChunk], uint4 (&v)[kChunk][4]) {
-    const int b = blk * kRowsPerWg + bl;
-    const int64_t base = ((int64_t)(b < batch ? b : 0) * n_heads + h) * num_splits;
+    const int b = blk * kRows + bl;
+    if (b >= batch || n_my == 0) {  // a row past the batch (or a group without splits) loads nothing
 #pragma unroll
-    for (int q = 0; q < kChunk; ++q) ls[q] = lse_partial[base + min(q, num_splits - 1)];  // masked at use
+      for (int q = 0; q < kChunk; ++q) {
+        ls[q] = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[q][k] = make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
+    const int64_t base = ((int64_t)b * n_heads + h) * num_splits;
+#pragma unroll
+    for (int q = 0; q < kChunk; ++q) ls[q] = lse_partial[base + sidx(min(q, n_my - 1))];  // masked at use
 #pragma unroll
     for (int q = 0; q < kChunk; ++q) {
-      const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + min(q, num_splits - 1)) * kDc + c0);
+      const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + sidx(min(q, n_my - 1))) * kDc + c0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[q][k] = src[k];
     }
@@ -85,27 +105,35 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
   };
 
   auto process_block = [&](int blk) {
-    const int b0 = blk * kRowsPerWg;
+    const int b0 = blk * kRows;
     // ---- 1. merge the splits (fp32) and stage the merged latent as bf16 hi + lo
     {
       const int b = b0 + bl;
-      const bool bok = b < batch;
+      const bool bok = b < batch && n_my > 0;
       const int64_t base = ((int64_t)(bok ? b : 0) * n_heads + h) * num_splits;
 #pragma unroll
-      for (int q = 0; q < kChunk; ++q) ls[q] = q < num_splits ? ls[q] : -INFINITY;
+      for (int q = 0; q < kChunk; ++q) ls[q] = q < n_my ? ls[q] : -INFINITY;
       float m = -INFINITY;
 #pragma unroll
       for (int q = 0; q < kChunk; ++q) m = fmaxf(m, ls[q]);
-      for (int s = kChunk; s < num_splits; ++s) m = fmaxf(m, lse_partial[base + s]);
+      if (bok)
+        for (int j = kChunk; j < n_my; ++j) m = fmaxf(m, lse_partial[base + sidx(j)]);
       float z = 0.f;
-      if (m != -INFINITY) {
+      if (bok && m != -INFINITY) {
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) z += ls[q] == -INFINITY ? 0.f : __expf(ls[q] - m);
-        for (int s = kChunk; s < num_splits; ++s) z += __expf(lse_partial[base + s] - m);
+        for (int j = kChunk; j < n_my; ++j) z += __expf(lse_partial[base + sidx(j)] - m);
       }
-      if ((tid & 15) == 0 && bok && lse_out)
-        lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
-      const float inv_z = (m == -INFINITY) ? 0.f : 1.f / z;
+      if constexpr (kGroups == 1) {
+        if ((tid & 15) == 0 && bok && lse_out)
+          lse_out[(int64_t)b * n_heads + h] = (m == -INFINITY) ? -INFINITY : m + __logf(z);
+      } else if ((tid & 15) == 0) {
+        stat_lds[2 * slot] = m;
+        stat_lds[2 * slot + 1] = z;
+      }
+      // one group: weights normalised here; several: sums relative to the group's own max, normalised
+      // when the groups meet
+      const float inv_z = (m == -INFINITY) ? 0.f : (kGroups == 1 ? 1.f / z : 1.f);
       float acc[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) acc[k] = 0.f;
@@ -125,12 +153,12 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
 #pragma unroll
         for (int q = 0; q < kChunk; ++q) accumulate(ls[q] == -INFINITY ? 0.f : __expf(ls[q] - m) * inv_z, v[q]);
         // further splits, kChunk at a time, every load of a chunk issued before the first multiply-add
-        for (int s0 = kChunk; s0 < num_splits; s0 += kChunk) {
+        for (int j0 = kChunk; j0 < n_my; j0 += kChunk) {
 #pragma unroll
           for (int q = 0; q < kChunk; ++q) {
-            const int s = min(s0 + q, num_splits - 1);
+            const int s = sidx(min(j0 + q, n_my - 1));
             const float l = lse_partial[base + s];
-            ls[q] = s0 + q < num_splits ? l : -INFINITY;
+            ls[q] = j0 + q < n_my ? l : -INFINITY;
             const uint4* src = reinterpret_cast<const uint4*>(o_partial + (base + s) * kDc + c0);
 #pragma unroll
             for (int k = 0; k < 4; ++k) v[q][k] = src[k];
@@ -139,8 +167,39 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
           for (int q = 0; q < kChunk; ++q) accumulate(ls[q] == -INFINITY ? 0.f : __expf(ls[q] - m) * inv_z, v[q]);
         }
       }
-      char* hrow = hi_lds + bl * kPitch + c0 * 2;
-      char* lrow = lo_lds + bl * kPitch + c0 * 2;
+      const int row = bl;  // the block row (MFMA column) this thread stages
+      if constexpr (kGroups > 1) {
+        // the groups of a sequence meet: group g's sums scaled by exp(m_g - M), divided by the total
+        // weight; the group-0 slot of each sequence stages it (rows kRows .. 15 of the staging tile
+        // feed MFMA columns that are never stored, and columns do not mix)
+#pragma unroll
+        for (int k = 0; k < 32; ++k) red_lds[slot * kDc + c0 + k] = acc[k];
+        __syncthreads();
+        if (grp == 0) {
+          float mg[kGroups], M = -INFINITY;
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) M = fmaxf(M, mg[g] = stat_lds[2 * (slot + g)]);
+          float wg[kGroups], Z = 0.f;
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) {
+            wg[g] = mg[g] == -INFINITY ? 0.f : __expf(mg[g] - M);
+            Z += wg[g] * stat_lds[2 * (slot + g) + 1];
+          }
+          const float iz = M == -INFINITY ? 0.f : 1.f / Z;
+#pragma unroll
+          for (int k = 0; k < 32; ++k) {
+            float t = 0.f;
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) t = fmaf(wg[g], red_lds[(slot + g) * kDc + c0 + k], t);
+            acc[k] = t * iz;
+          }
+          if ((tid & 15) == 0 && b < batch && lse_out)
+            lse_out[(int64_t)b * n_heads + h] = (M == -INFINITY) ? -INFINITY : M + __logf(Z);
+        }
+      }
+      char* hrow = hi_lds + row * kPitch + c0 * 2;
+      char* lrow = lo_lds + row * kPitch + c0 * 2;
+      if (kGroups == 1 || grp == 0)
 #pragma unroll
       for (int k = 0; k < 32; k += 8) {
         uint32_t hw[4], lw[4];
@@ -174,7 +233,7 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_kernel(int batch, int n_h
       }
       // D of tile vt: lane holds sequence b0 + lane % 16 and output dims 32 wave + 16 vt + 4 (lane / 16) + (0..3)
       const int b = b0 + (lane & 15);
-      if (b < batch) {
+      if ((lane & 15) < kRows && b < batch) {
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt) {
           uint16_t* dst = out + ((int64_t)b * n_heads + h) * kDv + 32 * wave + 16 * vt + 4 * (lane >> 4);
@@ -213,14 +272,21 @@ hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t
                           const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
                           hipStream_t stream) {
   if (batch == 0) return hipSuccess;
+  // up to 4 sequences with 16 splits or more: four thread groups per sequence, one block
+  if (batch <= kRowsPerWg / 4 && num_splits >= 16) {
+    // chunks of 4 splits per group: with 8 the registers of the group merge spill
+    hipLaunchKernelGGL((combine_mfma_kernel<4, 4>), dim3(n_heads, 1), dim3(256), 0, stream, batch, n_heads, num_splits,
+                       1, o_partial, lse_partial, w_uv, out, lse_out);
+    return hipGetLastError();
+  }
   // 16-sequence blocks per work-group: one for small batches; with many rows (prefill) enough that
   // about 512 work-groups each load their W_UV rows once
   const int64_t nblk = (batch + kRowsPerWg - 1) / kRowsPerWg;
   const int64_t bpw = std::max<int64_t>(1, (nblk * n_heads + 511) / 512);
   const int64_t yb = (nblk + bpw - 1) / bpw;
   if (yb > 65535) return hipErrorInvalidValue;
-#define MLA_LAUNCH_COMBINE(C_)                                                                                   \
-  hipLaunchKernelGGL(combine_mfma_kernel<C_>, dim3(n_heads, (unsigned)yb), dim3(256), 0, stream, batch, n_heads, \
+#define MLA_LAUNCH_COMBINE(C_)                                                                                      \
+  hipLaunchKernelGGL((combine_mfma_kernel<C_, 1>), dim3(n_heads, (unsigned)yb), dim3(256), 0, stream, batch, n_heads, \
                      num_splits, (int)bpw, o_partial, lse_partial, w_uv, out, lse_out)
   if (num_splits <= 1)
     MLA_LAUNCH_COMBINE(1);

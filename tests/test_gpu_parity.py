@@ -139,6 +139,39 @@ def test_partials_and_combine_match_oracle():
     assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
 
 
+@pytest.mark.parametrize("batch,ns", [(1, 16), (3, 19), (4, 64), (5, 33)])
+def test_combine_many_splits_small_batch(batch, ns):
+    """The combine on host-drawn partials: up to 4 sequences with 16 splits or more take the kernel
+    whose four thread groups each merge a quarter of a sequence's splits and meet in LDS (5 rows
+    take the one-group kernel). Empty splits (lse = -inf, zero partial) sit at the ends and in the
+    middle; with more than one sequence the last has only empty splits (its output is 0, its lse
+    -inf)."""
+    say(f"[combine] batch={batch} splits={ns}")
+    case = make_case("combine_groups", 97, 32, [64] * batch, paged=False)
+    dc = DeviceCase(case)
+    dc.alloc_decode(ns)
+    rng = np.random.default_rng(1000 + 7 * batch + ns)
+    H = case.n_heads
+    l_ref = rng.uniform(-3.0, 3.0, (batch, H, ns))
+    l_ref[:, :, rng.choice(ns, size=ns // 3, replace=False)] = -np.inf
+    l_ref[:, :, -1] = -np.inf
+    if batch > 1:
+        l_ref[-1] = -np.inf
+    o_bf = O.f64_to_bf16(rng.standard_normal((batch, H, ns, 512)))
+    o_bf[np.isneginf(l_ref)] = 0
+    o_in = torch.from_numpy(o_bf.view(np.int16)).cuda()
+    l_in = torch.from_numpy(l_ref.astype(np.float32)).cuda()
+    lib.decode_combine(dc.dims, batch, ns, o_in, l_in, dc.w_uv, dc.out, dc.lse)
+    torch.cuda.synchronize()
+    ref, rl = O.combine(O.bf16_to_f64(o_bf), l_ref.astype(np.float32).astype(np.float64), case.w_uv)
+    got, lse = to_f64(dc.out), dc.lse.cpu().numpy()
+    live = batch - 1 if batch > 1 else 1
+    if batch > 1:
+        assert np.all(got[-1] == 0) and np.all(np.isneginf(lse[-1]))
+    assert_close(got[:live], ref[:live], "combine")
+    assert np.max(np.abs(lse[:live] - rl[:live])) <= 1e-4
+
+
 def test_paged_equals_contiguous_and_block_permutation_bitwise():
     say("[decode] paged == contiguous == permuted blocks, bit for bit")
     lens = [700, 129, 64]
