@@ -172,6 +172,27 @@ def test_combine_many_splits_small_batch(batch, ns):
     assert np.max(np.abs(lse[:live] - rl[:live])) <= 1e-4
 
 
+@pytest.mark.parametrize("st,ns", [(320, 1), (64, 5)])
+def test_decode_many_short_sequences(st, ns):
+    """1500 paged sequences of 1..300 tokens: the combine runs several 16-sequence blocks per
+    work-group (with one split the next block's partials load during the current block; with five,
+    block by block); sampled sequences, every head, against the oracle."""
+    say(f"[decode] 1500 short sequences, split {st} x {ns}")
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 301, 1500).tolist()
+    case = make_case("many_short", 78, 16, lens, paged=True, spare_blocks=4)
+    dc, out, lse = run_decode(case, st, ns)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    seqs = sorted(set([0, 1, 15, 16, 17, 1499] + rng.integers(0, 1500, 40).tolist()))
+    heads = list(range(16))
+    cache, q_rot = oracle_cache(case)
+    ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
+                       case.w_uk, case.w_uv, seqs=seqs, heads=heads)
+    sel = np.ix_(seqs, heads)
+    assert_close(out[sel], ref[sel], "many short sequences")
+    assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
+
+
 def test_paged_equals_contiguous_and_block_permutation_bitwise():
     say("[decode] paged == contiguous == permuted blocks, bit for bit")
     lens = [700, 129, 64]
