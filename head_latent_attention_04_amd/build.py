@@ -64,5 +64,42 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime (preloaded into an uninstrumented host process)."""
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("AddressSanitizer runtime not found next to hipcc")
+    return hits[-1]
+
+
+def build_host_asan(out_dir: str) -> str:
+    """The library with its host-side C-ABI layer (argument validation, workspace layout, launch
+    set-up) built under AddressSanitizer; device code and the other objects are the regular build's.
+    Returns the path of the shared library written to out_dir."""
+    os.makedirs(out_dir, exist_ok=True)
+    api = os.path.join(CSRC, "mla_api.hip")
+    others = [s for s in sorted(glob.glob(os.path.join(CSRC, "*.hip"))) if s != api]
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in others]
+    if not all(os.path.exists(o) for o in objs):
+        os.makedirs(BUILD, exist_ok=True)
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(others))) as ex:
+            objs = list(ex.map(_compile, others))
+    api_obj = os.path.join(out_dir, "mla_api_asan.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    cmd = [hipcc(), *common_flags(), "-O1", "-g", *san, "-c", api, "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    lib = os.path.join(out_dir, "libmla_asan.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-shared-libasan", "-o", lib, api_obj, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build()

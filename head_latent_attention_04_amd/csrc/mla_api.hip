@@ -11,6 +11,10 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int32_t kMaxSplitTokens = 0x7FFFFFC0;  // largest block multiple: one split per row
+constexpr int32_t kMaxPrefillTokens = 1 << 24;    // query tokens of one mla_chunked_prefill call
+
+// true if p is a multiple of n bytes (n a power of two); NULL counts as aligned (optional pointers)
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 
 int check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_NULL;
@@ -24,9 +28,12 @@ int check_dims(const mla_dims* d) {
   return MLA_OK;
 }
 
+// The cache rows are read and written in 16-byte pieces (and copied into LDS by 16-byte buffer
+// loads), the block table as int32.
 int check_cache(const mla_cache* c) {
   if (!c || !c->data) return MLA_ERR_NULL;
   if (c->num_blocks <= 0 || c->max_blocks_per_seq <= 0) return MLA_ERR_BAD_ARG;
+  if (!aligned(c->data, 16) || !aligned(c->block_table, 4)) return MLA_ERR_BAD_ARG;
   return MLA_OK;
 }
 
@@ -41,6 +48,7 @@ int check_splits(const mla_dims* d, int32_t batch, int32_t split_tokens, int32_t
 mla::CacheView view(const mla_cache* c) { return mla::CacheView{c->data, c->block_table, c->max_blocks_per_seq}; }
 
 int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
 
 struct PrefillWorkspace {
   size_t q_abs, o_lat, lse, total;
@@ -80,6 +88,9 @@ int mla_rope_append(const mla_dims* dims, const mla_cache* cache, int32_t num_to
   if (num_tokens < 0) return MLA_ERR_BAD_ARG;
   if (num_tokens == 0) return MLA_OK;
   if (!token_seq || !token_pos || !c_kv || !k_rope) return MLA_ERR_NULL;
+  if (!aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(c_kv, 16) || !aligned(k_rope, 4) ||
+      !aligned(q_rope_inout, 16))
+    return MLA_ERR_BAD_ARG;
   return launched(mla::launch_rope_append(view(cache), dims->n_heads, num_tokens, token_seq, token_pos, c_kv, k_rope,
                                           q_rope_inout, dims->rope_theta, stream));
 }
@@ -261,7 +272,8 @@ int mla_absorb(const mla_dims* dims, int32_t rows, const uint16_t* q_nope, const
   if (rows == 0) return MLA_OK;
   if (!q_nope || !q_rope || !w_uk || !workspace) return MLA_ERR_NULL;
   if (workspace_bytes < mla_decode_workspace_size(dims, rows)) return MLA_ERR_BAD_ARG;
-  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  if (!aligned(workspace, 256) || !aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16))
+    return MLA_ERR_BAD_ARG;
   return launched(mla::launch_absorb(rows, dims->n_heads, q_nope, q_rope, w_uk, static_cast<uint16_t*>(workspace),
                                      false, stream));
 }
@@ -278,7 +290,9 @@ int mla_rope_append_absorb(const mla_dims* dims, const mla_cache* cache, int32_t
   if (!token_seq || !token_pos || !c_kv || !k_rope || !q_rope_inout || !q_nope || !w_uk || !workspace)
     return MLA_ERR_NULL;
   if (workspace_bytes < mla_decode_workspace_size(dims, num_tokens)) return MLA_ERR_BAD_ARG;
-  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  if (!aligned(workspace, 256) || !aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(c_kv, 16) ||
+      !aligned(k_rope, 4) || !aligned(q_rope_inout, 16) || !aligned(q_nope, 16) || !aligned(w_uk, 16))
+    return MLA_ERR_BAD_ARG;
   return launched(mla::launch_rope_absorb(view(cache), dims->n_heads, num_tokens, token_seq, token_pos, c_kv, k_rope,
                                           q_rope_inout, dims->rope_theta, q_nope, w_uk,
                                           static_cast<uint16_t*>(workspace), stream));
@@ -294,7 +308,8 @@ int mla_decode_attend(const mla_dims* dims, const mla_cache* cache, int32_t batc
   if (batch == 0) return MLA_OK;
   if (!seq_lens || !workspace || !o_partial || !lse_partial) return MLA_ERR_NULL;
   if (workspace_bytes < mla_decode_workspace_size(dims, batch)) return MLA_ERR_BAD_ARG;
-  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  if (!aligned(workspace, 256) || !aligned(seq_lens, 4) || !aligned(o_partial, 16) || !aligned(lse_partial, 4))
+    return MLA_ERR_BAD_ARG;
   return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch,
                                         static_cast<const uint16_t*>(workspace), true, dims->scale, split_tokens,
                                         num_splits, o_partial, lse_partial, stream));
@@ -311,7 +326,9 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   if (batch == 0) return MLA_OK;
   if (!seq_lens || !q_nope || !q_rope || !w_uk || !workspace || !o_partial || !lse_partial) return MLA_ERR_NULL;
   if (workspace_bytes < mla_decode_workspace_size(dims, batch)) return MLA_ERR_BAD_ARG;
-  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  if (!aligned(workspace, 256) || !aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) ||
+      !aligned(seq_lens, 4) || !aligned(o_partial, 16) || !aligned(lse_partial, 4))
+    return MLA_ERR_BAD_ARG;
   st = mla_absorb(dims, batch, q_nope, q_rope, w_uk, workspace, workspace_bytes, stream);
   if (st != MLA_OK) return st;
   return mla_decode_attend(dims, cache, batch, seq_lens, workspace, workspace_bytes, split_tokens, num_splits,
@@ -327,6 +344,8 @@ int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t ba
   if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
   if (batch == 0) return MLA_OK;
   if (!seq_lens || !q_abs || !o_partial || !lse_partial) return MLA_ERR_NULL;
+  if (!aligned(seq_lens, 4) || !aligned(q_abs, 16) || !aligned(o_partial, 16) || !aligned(lse_partial, 4))
+    return MLA_ERR_BAD_ARG;
   return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch, q_abs, false,
                                         dims->scale, split_tokens, num_splits, o_partial, lse_partial, stream));
 }
@@ -339,6 +358,9 @@ int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, 
   if (batch < 0 || num_splits <= 0 || num_splits > 65535) return MLA_ERR_BAD_ARG;
   if (batch == 0) return MLA_OK;
   if (!o_partial || !lse_partial || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned(o_partial, 16) || !aligned(lse_partial, 4) || !aligned(w_uv, 16) || !aligned(out, 8) ||
+      !aligned(lse_out, 4))
+    return MLA_ERR_BAD_ARG;
   return launched(mla::launch_combine(batch, dims->n_heads, num_splits, o_partial, lse_partial, w_uv, out, lse_out,
                                       stream));
 }
@@ -355,12 +377,15 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if ((st = check_cache(cache)) != MLA_OK) return st;
-  if (batch < 0 || total_q < 0 || max_q_len < 0 || total_q > 65535) return MLA_ERR_BAD_ARG;
+  // one attention work-group per (query token, group of 128 heads): the grid stays far below 2^31
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || total_q > kMaxPrefillTokens) return MLA_ERR_BAD_ARG;
   if (batch == 0 || total_q == 0) return MLA_OK;
   if (!seq_lens || !cu_q_lens || !q_nope || !q_rope || !w_uk || !w_uv || !workspace || !out) return MLA_ERR_NULL;
   PrefillWorkspace lay = prefill_layout(dims, total_q);
   if (workspace_bytes < lay.total) return MLA_ERR_BAD_ARG;
-  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_BAD_ARG;
+  if (!aligned(workspace, 256) || !aligned(seq_lens, 4) || !aligned(cu_q_lens, 4) || !aligned(q_nope, 16) ||
+      !aligned(q_rope, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) || !aligned(out, 8) || !aligned(lse_out, 4))
+    return MLA_ERR_BAD_ARG;
   char* ws = static_cast<char*>(workspace);
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + lay.q_abs);
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + lay.o_lat);

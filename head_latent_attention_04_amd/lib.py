@@ -15,7 +15,8 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIBRARY names another build of the same library (the host-sanitizer build the CPU tests make)
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_HERE, "libmla.so")
 
 D_C, D_ROPE, D_NOPE, D_V, BLOCK = 512, 64, 128, 128, 64
 ROW = D_C + D_ROPE
@@ -31,6 +32,8 @@ class MlaDims(ctypes.Structure):
 
 
 class MlaCache(ctypes.Structure):
+    """The C descriptor of a paged cache. Built by make_cache, it also keeps the tensors whose device
+    pointers it holds (`tensors`), so they cannot be freed and reused while the descriptor lives."""
     _fields_ = [("data", _vp), ("num_blocks", _i64), ("block_table", _vp), ("max_blocks_per_seq", _i32)]
 
 
@@ -139,17 +142,29 @@ def _stream(stream) -> Optional[int]:
 def make_cache(data: torch.Tensor, block_table: Optional[torch.Tensor], max_blocks_per_seq: int) -> MlaCache:
     """data: [num_blocks, 64, 576] bf16 (or its int16 view); block_table: [batch, max_blocks] int32 or None.
 
-    The descriptor holds raw device pointers: the caller keeps both tensors alive while it is used."""
+    The returned descriptor holds the device pointers of both tensors and a reference to each
+    tensor, so the memory stays allocated for as long as the descriptor is alive, whatever the
+    caller does with its own references."""
     if data.dim() != 3 or data.shape[1] != BLOCK or data.shape[2] != ROW:
         raise ValueError("cache data must be [num_blocks, 64, 576]")
-    return MlaCache(_ptr(data, "cache", BF16), data.shape[0], _ptr(block_table, "block_table", I32),
-                    max_blocks_per_seq)
+    if block_table is not None and (block_table.dim() != 2 or block_table.shape[1] != max_blocks_per_seq):
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    c = MlaCache(_ptr(data, "cache", BF16), data.shape[0], _ptr(block_table, "block_table", I32), max_blocks_per_seq)
+    c.tensors = (data, block_table)
+    return c
+
+
+def _cache(cache: MlaCache):
+    """byref of a descriptor made by make_cache (one without its tensors could point at freed memory)."""
+    if not isinstance(cache, MlaCache) or getattr(cache, "tensors", None) is None:
+        raise ValueError("pass the cache descriptor returned by make_cache")
+    return ctypes.byref(cache)
 
 
 def rope_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_kv, k_rope, q_rope=None, stream=None):
     T = token_seq.numel()
     st = load().mla_rope_append(
-        ctypes.byref(dims), ctypes.byref(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        ctypes.byref(dims), _cache(cache), T, _ptr(token_seq, "token_seq", I32, T),
         _ptr(token_pos, "token_pos", I32, T), _ptr(c_kv, "c_kv", BF16, T * dims.d_c),
         _ptr(k_rope, "k_rope", BF16, T * dims.d_rope),
         _ptr(q_rope, "q_rope", BF16, T * dims.n_heads * dims.d_rope), _stream(stream))
@@ -237,7 +252,7 @@ def chunked_prefill_expanded(dims: MlaDims, cache: MlaCache, seq_lens, cu_q_lens
     H = dims.n_heads
     Tq = q_nope.shape[0]
     st = load().mla_chunked_prefill_expanded(
-        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
         _ptr(cu_q_lens, "cu_q_lens", I32, B + 1), Tq, max_q_len, max_seq_len,
         _ptr(q_nope, "q_nope", BF16, Tq * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, Tq * H * dims.d_rope),
         _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c),
@@ -255,7 +270,7 @@ def kv_down_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, x, w_dk
     T = token_seq.numel()
     dim = x.shape[1] if x.dim() == 2 else 0
     st = load().mla_kv_down_append(
-        ctypes.byref(dims), ctypes.byref(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        ctypes.byref(dims), _cache(cache), T, _ptr(token_seq, "token_seq", I32, T),
         _ptr(token_pos, "token_pos", I32, T), _ptr(x, "x", BF16, T * dim), dim,
         _ptr(w_dkv, "w_dkv", BF16, (dims.d_c + dims.d_rope) * dim), _ptr(gamma, "gamma", BF16, dims.d_c), eps,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -278,7 +293,7 @@ def decode(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split
     B = seq_lens.numel()
     H = dims.n_heads
     st = load().mla_decode(
-        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
         _ptr(q_nope, "q_nope", BF16, B * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, B * H * dims.d_rope),
         _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), split_tokens, num_splits,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
@@ -302,7 +317,7 @@ def rope_append_absorb(dims: MlaDims, cache: MlaCache, token_seq, token_pos, c_k
     T = token_seq.numel()
     H = dims.n_heads
     st = load().mla_rope_append_absorb(
-        ctypes.byref(dims), ctypes.byref(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        ctypes.byref(dims), _cache(cache), T, _ptr(token_seq, "token_seq", I32, T),
         _ptr(token_pos, "token_pos", I32, T), _ptr(c_kv, "c_kv", BF16, T * dims.d_c),
         _ptr(k_rope, "k_rope", BF16, T * dims.d_rope), _ptr(q_rope, "q_rope", BF16, T * H * dims.d_rope),
         _ptr(q_nope, "q_nope", BF16, T * H * dims.d_nope), _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c),
@@ -315,7 +330,7 @@ def decode_attend(dims: MlaDims, cache: MlaCache, seq_lens, workspace, split_tok
     B = seq_lens.numel()
     H = dims.n_heads
     st = load().mla_decode_attend(
-        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), split_tokens, num_splits,
         _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
@@ -327,7 +342,7 @@ def decode_absorbed(dims: MlaDims, cache: MlaCache, seq_lens, q_abs, split_token
     B = seq_lens.numel()
     H = dims.n_heads
     st = load().mla_decode_absorbed(
-        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
         _ptr(q_abs, "q_abs", BF16, B * H * (dims.d_c + dims.d_rope)), split_tokens, num_splits,
         _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
@@ -355,7 +370,7 @@ def chunked_prefill(dims: MlaDims, cache: MlaCache, seq_lens, cu_q_lens, max_q_l
     H = dims.n_heads
     Tq = q_nope.shape[0]
     st = load().mla_chunked_prefill(
-        ctypes.byref(dims), ctypes.byref(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
         _ptr(cu_q_lens, "cu_q_lens", I32, B + 1), Tq, max_q_len,
         _ptr(q_nope, "q_nope", BF16, Tq * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, Tq * H * dims.d_rope),
         _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c),

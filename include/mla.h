@@ -33,6 +33,12 @@
  *     0 <= seq_len <= max_blocks_per_seq * block_size, positions must be < seq_len.
  *   - Supported shapes: d_c = 512, d_rope = 64, d_nope = 128, d_v = 128, block_size = 64,
  *     n_heads a positive multiple of 16. Others return MLA_ERR_UNSUPPORTED.
+ *   - Alignment (checked on the host; a misaligned pointer returns MLA_ERR_BAD_ARG before any HIP
+ *     call): the kernels move bf16 tensors in 16-byte pieces, so unless an entry point states
+ *     otherwise every bf16 tensor pointer (cache data, c_kv, q_nope, q_rope, q_abs, w_uk, w_uv,
+ *     o_partial) must be 16-byte aligned, bf16 outputs of d_v elements per row (out) 8-byte
+ *     aligned, int32 and fp32 pointers 4-byte aligned, k_rope 4-byte aligned, and workspaces
+ *     256-byte aligned. Optional pointers that are NULL are not checked.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -63,7 +69,7 @@ typedef struct mla_dims {
   float rope_theta;   /* RoPE base, normally 10000; must be > 1 */
 } mla_dims;
 
-/* Paged latent cache. Row of token t of sequence b lives at
+/* Paged latent cache (data 16-byte aligned, block_table 4-byte aligned). Row of token t of sequence b lives at
  *   data + ((int64)phys * block_size + t % block_size) * (d_c + d_rope),
  *   phys = block_table[b * max_blocks_per_seq + t / block_size]   (paged), or
  *   phys = b * max_blocks_per_seq + t / block_size                 (block_table == NULL: contiguous).
@@ -236,6 +242,7 @@ size_t mla_chunked_prefill_workspace_size(const mla_dims* dims, int32_t total_q)
  *   q_nope    [total_q, n_heads, d_nope] bf16;  q_rope [total_q, n_heads, d_rope] bf16 rotated at p
  *   w_uk, w_uv as for decode;  out [total_q, n_heads, d_v] bf16;  lse_out [total_q, n_heads] fp32 or NULL
  *   workspace >= mla_chunked_prefill_workspace_size(dims, total_q) bytes, 256-byte aligned
+ *   total_q <= 16777216; q_nope, q_rope, w_uk, w_uv 16-byte aligned, out 8-byte aligned
  * ------------------------------------------------------------------------------------------- */
 int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t batch,
                         const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t total_q,

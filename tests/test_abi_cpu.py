@@ -179,3 +179,77 @@ def test_query_path_validation_and_workspace():
     # cos/sin pairs per token
     assert lib.query_absorbed_workspace_size(d, 32, 4096, 512) == 16 * 32 * 512 * 4 + 32 * 512 * 2 + 32 * 32 * 16
     assert lib.query_absorbed_workspace_size(d, 32, 100, 512) == 0
+
+
+MIS16 = FAKE + 8   # 8-byte aligned, not 16
+MIS8 = FAKE + 4    # 4-byte aligned, not 8
+MIS4 = FAKE + 2    # 2-byte aligned, not 4
+
+
+def test_misaligned_pointers_are_rejected_before_any_launch():
+    """Every pointer a kernel reads or writes in 16-, 8- or 4-byte pieces is checked on the host:
+    a misaligned one returns MLA_ERR_BAD_ARG (nothing is dereferenced: FAKE is not device memory)."""
+    L = lib.load()
+    d = D()
+    # cache descriptor: data in 16-byte pieces, the block table as int32
+    assert rope(d, cache(data=MIS16)) == lib.MLA_ERR_BAD_ARG
+    assert rope(d, lib.MlaCache(FAKE, 4, MIS4, 2)) == lib.MLA_ERR_BAD_ARG
+    assert dec(d, cache(data=MIS16)) == lib.MLA_ERR_BAD_ARG
+    # mla_rope_append: token_seq, token_pos, c_kv, k_rope, q_rope_inout
+    for i, bad in enumerate((MIS4, MIS4, MIS16, MIS4)):
+        ptrs = [FAKE] * 4
+        ptrs[i] = bad
+        assert rope(d, cache(), ptrs=tuple(ptrs)) == lib.MLA_ERR_BAD_ARG, i
+    assert L.mla_rope_append(ctypes.byref(d), ctypes.byref(cache()), 1, FAKE, FAKE, FAKE, FAKE, MIS16, None) \
+        == lib.MLA_ERR_BAD_ARG
+    # mla_decode: seq_lens, q_nope, q_rope, w_uk, then the partials
+    for i, bad in enumerate((MIS4, MIS16, MIS16, MIS16)):
+        ptrs = [FAKE] * 4
+        ptrs[i] = bad
+        assert dec(d, cache(), ptrs=tuple(ptrs)) == lib.MLA_ERR_BAD_ARG, i
+    assert dec(d, cache(), part=(MIS16, FAKE)) == lib.MLA_ERR_BAD_ARG
+    assert dec(d, cache(), part=(FAKE, MIS4)) == lib.MLA_ERR_BAD_ARG
+    # mla_absorb (q_nope, q_rope, w_uk) and mla_rope_append_absorb (..., q_rope, q_nope, w_uk)
+    for i in range(3):
+        p = [FAKE] * 3
+        p[i] = MIS16
+        assert L.mla_absorb(ctypes.byref(d), 2, *p, FAKE, 1 << 30, None) == lib.MLA_ERR_BAD_ARG, i
+    for i in range(3):
+        p = [FAKE] * 3
+        p[i] = MIS16
+        assert L.mla_rope_append_absorb(ctypes.byref(d), ctypes.byref(cache()), 2, FAKE, FAKE, FAKE, FAKE, *p, FAKE,
+                                        1 << 30, None) == lib.MLA_ERR_BAD_ARG, i
+    # mla_decode_attend: the partials; mla_decode_absorbed: q_abs and the partials
+    assert L.mla_decode_attend(ctypes.byref(d), ctypes.byref(cache()), 2, FAKE, FAKE, 1 << 30, 64, 2, MIS16, FAKE,
+                               None) == lib.MLA_ERR_BAD_ARG
+    assert L.mla_decode_absorbed(ctypes.byref(d), ctypes.byref(cache()), 2, FAKE, MIS16, 64, 2, FAKE, FAKE, None) \
+        == lib.MLA_ERR_BAD_ARG
+    assert L.mla_decode_absorbed(ctypes.byref(d), ctypes.byref(cache()), 2, FAKE, FAKE, 64, 2, MIS16, FAKE, None) \
+        == lib.MLA_ERR_BAD_ARG
+    # mla_decode_combine: o_partial, lse_partial, w_uv, out, lse_out
+    for i, bad in enumerate((MIS16, MIS4, MIS16, MIS8, MIS4)):
+        p = [FAKE] * 5
+        p[i] = bad
+        assert L.mla_decode_combine(ctypes.byref(d), 2, 4, *p, None) == lib.MLA_ERR_BAD_ARG, i
+    # mla_chunked_prefill: seq_lens, cu_q_lens, q_nope, q_rope, w_uk, w_uv, ..., out, lse_out
+    for i, bad in enumerate((MIS4, MIS4, MIS16, MIS16, MIS16, MIS16, None, MIS8, MIS4)):
+        if bad is None:
+            continue
+        p = [FAKE] * 9
+        p[i] = bad
+        assert L.mla_chunked_prefill(ctypes.byref(d), ctypes.byref(cache()), 1, p[0], p[1], 4, 4, p[2], p[3], p[4],
+                                     p[5], FAKE, 1 << 30, p[7], p[8], None) == lib.MLA_ERR_BAD_ARG, i
+    # the same calls with every pointer aligned get past validation: with batch 0 / no tokens they are no-ops
+    assert L.mla_decode_combine(ctypes.byref(d), 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == lib.MLA_OK
+
+
+def test_prefill_token_limit():
+    """mla_chunked_prefill takes up to 2^24 query tokens in one call (one attention work-group per
+    token and head group keeps the grid far below 2^31); more is rejected on the host."""
+    L = lib.load()
+    d = D()
+    c = cache()
+    call = lambda T: L.mla_chunked_prefill(ctypes.byref(d), ctypes.byref(c), 1, FAKE, FAKE, T, 4, FAKE, FAKE,  # noqa
+                                           FAKE, FAKE, FAKE, 1 << 62, FAKE, None, None)
+    assert call((1 << 24) + 1) == lib.MLA_ERR_BAD_ARG
+    assert lib.chunked_prefill_workspace_size(d, 70000) >= 70000 * 128 * 576 * 2

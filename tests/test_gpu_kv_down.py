@@ -47,8 +47,8 @@ def run_case(seq_lens, new_lens, dim, seed):
     inp = make_kv_down_inputs(seed, T, dim)
     say(f"  T={T} dim={dim} blocks={num_blocks}")
     dims = lib.make_dims(128)
-    # every device buffer stays referenced until the call has finished: make_cache keeps only raw
-    # pointers, and memory torch frees is handed to the next allocation
+    # the inputs stay referenced until the call has finished (the cache descriptor keeps its own
+    # tensors; memory torch frees is handed to the next allocation)
     data = torch.full((num_blocks, 64, 576), BF16_NAN, dtype=torch.int16, device="cuda")
     table_d = _dev(table)
     cache = lib.make_cache(data, table_d, max_blocks)

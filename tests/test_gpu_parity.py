@@ -448,3 +448,31 @@ def test_decode_step_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(dc.out, ref_out), f"replay {rep}: out differs"
         assert torch.equal(dc.lse, ref_lse), f"replay {rep}: lse differs"
+
+
+def test_cache_descriptor_keeps_its_tensors():
+    """A cache descriptor built over tensors whose only references are the descriptor's own still
+    points at live memory: make_cache holds the tensors. New allocations of the same sizes (which
+    reuse freed memory first) are filled with garbage before the decode reads the cache."""
+    say("[decode] cache descriptor lifetime")
+    case = make_case("lifetime", 91, 32, [300, 64, 5], paged=True, spare_blocks=2)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.append_new()
+    cache = lib.make_cache(dc.cache_data.clone(), dc.table.clone(), case.max_blocks_per_seq)
+    torch.cuda.synchronize()
+    junk = [torch.full_like(dc.cache_data, 0x7FC0), torch.full_like(dc.table, 1 << 30)]
+    st, ns = 128, 3
+    dc.alloc_decode(ns)
+    o_part, lse_part = dc.partials
+    lib.decode(dc.dims, cache, dc.seq_lens, dc.q_nope, dc.q_rope, dc.w_uk, st, ns, dc._ws, o_part, lse_part)
+    lib.decode_combine(dc.dims, case.batch, ns, o_part, lse_part, dc.w_uv, dc.out, dc.lse)
+    torch.cuda.synchronize()
+    del junk
+    oc, q_rot = oracle_cache(case)
+    ref, rl = O.decode(oc, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
+                       case.w_uk, case.w_uv)
+    assert_close(to_f64(dc.out), ref, "descriptor lifetime")
+    with pytest.raises(ValueError):
+        lib.decode(dc.dims, lib.MlaCache(cache.data, cache.num_blocks, cache.block_table, cache.max_blocks_per_seq),
+                   dc.seq_lens, dc.q_nope, dc.q_rope, dc.w_uk, st, ns, dc._ws, o_part, lse_part)

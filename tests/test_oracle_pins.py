@@ -208,6 +208,34 @@ def pin_special_cases():
     assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
 
 
+def pin_identical_rows():
+    """Every cached row of a sequence the same (written straight into the cache): all scores are equal,
+    so the softmax is uniform, out = W_UV c and lse = s + ln L with s the one score. The query is
+    large (scores up to a few thousand, where exp without the max subtracted overflows or underflows)."""
+    rng = np.random.default_rng(12)
+    H, d_c, d_r, d_nope, d_v, bs = 3, 8, 4, 4, 4, 4
+    lens = np.array([7, 1, 12], np.int32)
+    maxb = 3
+    table = np.array([[2, 0, 7], [5, 1, 3], [4, 6, 8]], np.int32)
+    cache = np.full((9, bs, d_c + d_r), 0x7FC0, np.uint16)
+    rows = bf16_bits(rng.standard_normal((3, d_c + d_r)))
+    for b in range(3):
+        for t in range(int(lens[b])):
+            cache[table[b, t // bs], t % bs] = rows[b]
+    qn = bf16_bits(rng.standard_normal((3, H, d_nope)) * 2048.0)
+    qr = bf16_bits(rng.standard_normal((3, H, d_r)) * 2048.0)
+    wk = bf16_bits(rng.standard_normal((H, d_nope, d_c)))
+    wv = bf16_bits(rng.standard_normal((H, d_v, d_c)))
+    out, lse = O.decode(cache, table, maxb, lens, qn, qr, wk, wv)
+    for b in range(3):
+        c, kr = widen(rows[b][:d_c]), widen(rows[b][d_c:])
+        for h in range(H):
+            s = (widen(qn[b, h]) @ (widen(wk[h]) @ c) + widen(qr[b, h]) @ kr) / math.sqrt(d_nope + d_r)
+            assert np.allclose(out[b, h], widen(wv[h]) @ c, rtol=1e-13, atol=1e-13)
+            assert abs(lse[b, h] - (s + math.log(int(lens[b])))) <= 1e-12 * max(1.0, abs(s))
+    assert np.max(np.abs(lse)) > 750.0  # some scores lie beyond where an unshifted exp leaves fp64
+
+
 def pin_wuk_zero_matches_sdpa():
     """With W_UK = 0 only the shared RoPE key scores, so each head is single-KV-head attention:
     compare with torch's scaled_dot_product_attention in float64 (a library routine)."""
@@ -451,7 +479,8 @@ def pin_output_side():
 
 
 PINS = [pin_bf16_rounding, pin_rope_complex_form, pin_rope_invariants, pin_bruteforce_decode,
-        pin_bruteforce_prefill, pin_absorbed_equals_expanded, pin_special_cases, pin_wuk_zero_matches_sdpa,
+        pin_bruteforce_prefill, pin_absorbed_equals_expanded, pin_special_cases, pin_identical_rows,
+        pin_wuk_zero_matches_sdpa,
         pin_split_invariance, pin_prefill_equals_decodes, pin_slot_mapping, pin_closed_forms, pin_rms_norm,
         pin_kv_down, pin_query_path, pin_output_side]
 
@@ -555,7 +584,28 @@ def _mut_fold_head_order(monkeypatch):
     monkeypatch.setattr(O, "fold_output_weights", bad)
 
 
+def _mut_lse_without_max(monkeypatch):
+    orig = O.softmax_lse
+
+    def sl(sc, axis=-1):
+        p, lse = orig(sc, axis)
+        m = np.max(sc, axis=axis)
+        return p, np.where(np.isfinite(m), lse - m, lse)   # ln sum exp(s - m), the max never added back
+    monkeypatch.setattr(O, "softmax_lse", sl)
+
+
+def _mut_softmax_unshifted(monkeypatch):
+    def sl(sc, axis=-1):
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            e = np.exp(sc)                                  # no max subtracted
+            z = np.sum(e, axis=axis, keepdims=True)
+            return e / z, np.squeeze(np.log(z), axis=axis)
+    monkeypatch.setattr(O, "softmax_lse", sl)
+
+
 MUTANTS = [
+    (_mut_lse_without_max, [pin_identical_rows]),
+    (_mut_softmax_unshifted, [pin_identical_rows]),
     (_mut_fold_head_order, [pin_output_side]),
     (_mut_q_split_swapped, [pin_query_path]),
     (_mut_uqk_transposed, [pin_query_path]),
