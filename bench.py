@@ -20,7 +20,6 @@ kernel's roofline fraction and the fp64 CPU oracle's rate (on the host's cores) 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time

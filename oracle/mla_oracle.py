@@ -388,14 +388,14 @@ def prefill(cache, block_table, max_blocks, seq_lens, cu_q_lens, q_nope, q_rope,
             hh = hs[i:i + step]
             K, V = expand_kv(c, wk[hh], wv[hh])
             k_full = np.concatenate([K, np.broadcast_to(kr, (len(hh),) + kr.shape)], axis=2)   # [h, t, 192]
-            q_full = np.concatenate([qn[:, hh], qr[:, hh]], axis=2)                            # [j, h, 192]
-            s = np.einsum("jhd,htd->jht", q_full, k_full) * scale
-            s = np.where(mask[:, None, :], s, -np.inf)
+            q_full = np.concatenate([qn[:, hh], qr[:, hh]], axis=2).transpose(1, 0, 2)         # [h, j, 192]
+            s = np.matmul(q_full, k_full.transpose(0, 2, 1)) * scale                          # [h, j, t]
+            s = np.where(mask[None, :, :], s, -np.inf)
             p, l = softmax_lse(s)
-            o = np.einsum("jht,htd->jhd", p, V)
+            o = np.matmul(p, V)                                                               # [h, j, d_v]
             for a, j in enumerate(js):
-                out[j, hh] = o[a]
-                lse[j, hh] = l[a]
+                out[j, hh] = o[:, a]
+                lse[j, hh] = l[:, a]
     return out, lse
 
 
@@ -431,6 +431,78 @@ def decode_absorbed(cache, block_table, max_blocks, seq_lens, q_nope, q_rope, w_
         o_lat = p @ c                                                               # [h, d_c]
         out[b, hs] = np.einsum("hvc,hc->hv", wv[hs], o_lat)
         lse[b, hs] = l
+    return out, lse
+
+
+def _values(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) widened to float64; any other array taken as float64 values."""
+    x = np.asarray(x)
+    return bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def decode_from_absorbed(cache, block_table, max_blocks, seq_lens, q_abs, w_uv, scale: float,
+                         seqs=None, heads=None, return_latent: bool = False):
+    """Decode attention given the absorbed query rows, float64: the computation behind an entry point
+    that takes q_abs directly. q_abs [B, H, d_c + d_R] = [W_UK[h]^T q_nope | q_R rotated] per head
+    (bf16 bit patterns or float64 values); s_t = scale (q_abs . [c_t | k_R,t]) over t < L_b,
+    p = softmax(s), o_lat = sum_t p_t c_t, out = W_UV[h] o_lat.
+    ([P1] section 4: the absorbed query is scored directly against c^KV and W_UV follows the latent
+    reduction; [P3] "MLA的數學原理".) Returns out [B, H, d_v], lse [B, H] (and o_lat [B, H, d_c] if
+    return_latent); unselected rows are NaN.
+    """
+    qa = _values(q_abs)
+    B, H, row = qa.shape
+    d_c = np.asarray(w_uv).shape[2]
+    d_v = np.asarray(w_uv).shape[1]
+    wv = bf16_to_f64(w_uv)
+    out = np.full((B, H, d_v), np.nan)
+    lse = np.full((B, H), np.nan)
+    lat = np.full((B, H, d_c), np.nan)
+    hs = _as_list(heads, H)
+    for b in _as_list(seqs, B):
+        L = int(seq_lens[b])
+        if L == 0:
+            out[b, hs], lse[b, hs], lat[b, hs] = 0.0, -np.inf, 0.0
+            continue
+        rows = gather_rows(cache, block_table, max_blocks, b, L)                    # [L, d_c + d_R]
+        s = (qa[b, hs] @ rows.T) * scale                                            # [h, L]
+        p, l = softmax_lse(s)
+        o_lat = p @ rows[:, :d_c]                                                   # [h, d_c]
+        out[b, hs] = np.einsum("hvc,hc->hv", wv[hs], o_lat)
+        lse[b, hs] = l
+        lat[b, hs] = o_lat
+    return (out, lse, lat) if return_latent else (out, lse)
+
+
+def prefill_from_absorbed(cache, block_table, max_blocks, seq_lens, cu_q_lens, q_abs, w_uv, scale: float,
+                          rows_sel: Optional[Sequence[int]] = None, heads: Optional[Iterable[int]] = None):
+    """Causal chunked prefill given the absorbed query rows, float64. q_abs [Tq, H, d_c + d_R] (bf16 bit
+    patterns or float64 values); query j of sequence b sits at p = L_b - q_len_b + (j - cu_q_lens[b]) and
+    sees keys t <= p ([P3] "大模型的整體推理過程": masked self-attention); per head the score, softmax,
+    latent reduction and W_UV follow decode_from_absorbed. Returns out [Tq, H, d_v], lse [Tq, H]
+    (NaN where not selected).
+    """
+    qa = _values(q_abs)
+    Tq, H, row = qa.shape
+    d_c = np.asarray(w_uv).shape[2]
+    d_v = np.asarray(w_uv).shape[1]
+    wv = bf16_to_f64(w_uv)
+    out = np.full((Tq, H, d_v), np.nan)
+    lse = np.full((Tq, H), np.nan)
+    hs = _as_list(heads, H)
+    sel = set(range(Tq)) if rows_sel is None else set(int(r) for r in rows_sel)
+    for b in range(len(seq_lens)):
+        q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        L = int(seq_lens[b])
+        for j in range(q0, q1):
+            if j not in sel:
+                continue
+            n = L - (q1 - q0) + (j - q0) + 1                                      # keys 0 .. p
+            rows = gather_rows(cache, block_table, max_blocks, b, n)
+            s = (qa[j, hs] @ rows.T) * scale                                      # [h, n]
+            p, l = softmax_lse(s)
+            out[j, hs] = np.einsum("hvc,hc->hv", wv[hs], p @ rows[:, :d_c])
+            lse[j, hs] = l
     return out, lse
 
 

@@ -1,62 +1,24 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
 
-Tolerances (bf16 inputs, fp32 accumulation): relative Frobenius error <= 5e-3 and max abs
-error <= 2e-2 over each compared output tensor. The log-sum-exp is compared with an absolute
-tolerance of 1e-2 (natural log): the absorbed query is rounded to bf16 (relative error up to
-2^-9 per element), which moves a unit-variance score by about 1e-3 RMS (2^-9/sqrt(3) times
-scale * |q_abs . c|, about 0.9e-3 at these distributions) and at most 2^-9 * scale * sum|q_abs c|
-(about 2.3e-2); lse moves by at most the largest score error. 1e-2 is about ten RMS. Integer
-handling (slot placement, paging) is compared bit for bit.
+Gates are those of gpu_helpers: relative Frobenius error <= 5e-3 and max abs error <= 2e-2 over each
+compared output tensor; the log-sum-exp within 1e-3 of the fp64 lse of the bf16-rounded absorbed query
+(the kernels' score operand) and within 1e-2 of the exact one. Integer handling (slot placement,
+paging) is compared bit for bit.
 """
 import numpy as np
 import pytest
 import torch
 
+from gpu_helpers import (SCALE, assert_close, assert_lse, decode_lse_of_rounded_query, oracle_cache,
+                         prefill_lse_of_rounded_query, run_decode, say)
 from head_latent_attention_04_amd import lib
 from head_latent_attention_04_amd.runner import DeviceCase, to_f64
 from oracle import mla_oracle as O
-from workloads import BF16_NAN, make_case, make_config
+from workloads import BF16_NAN, make_case
 
 pytestmark = pytest.mark.gpu
 
-REL_FRO = 5e-3
-MAX_ABS = 2e-2
-LSE_ABS = 1e-2
-
-
-def say(*a):
-    print(*a, flush=True)
-
-
-def oracle_cache(case):
-    cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
-    cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
-                             case.c_kv, case.k_rope)
-    q_rot = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(case.q_rope), case.q_positions()[:, None]))
-    return cache, q_rot
-
-
-def assert_close(got, ref, what):
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = got - ref
-    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
-    mx = np.max(np.abs(err)) if err.size else 0.0
-    say(f"  {what}: rel_fro={rel:.3e} max_abs={mx:.3e}")
-    assert rel <= REL_FRO, f"{what}: relative Frobenius error {rel:.3e} > {REL_FRO}"
-    assert mx <= MAX_ABS, f"{what}: max abs error {mx:.3e} > {MAX_ABS}"
-
-
-def run_decode(case, split_tokens=None, num_splits=None, dc=None):
-    if dc is None:
-        dc = DeviceCase(case)
-        dc.fill_history()
-        dc.append_new()
-    if split_tokens is None:
-        split_tokens, num_splits = dc.plan()
-    dc.alloc_decode(num_splits)
-    dc.decode(split_tokens, num_splits)
-    torch.cuda.synchronize()
-    return dc, to_f64(dc.out), dc.lse.cpu().numpy().astype(np.float64)
+LSE_ABS = 1e-2   # lse against the exact fp64 value where no rounded-query reference is formed
 
 
 SMALL = [
@@ -81,7 +43,7 @@ def test_decode_matches_oracle(name, H, lens, paged, st):
     ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
                        case.w_uk, case.w_uv)
     assert_close(out, ref, name)
-    assert np.max(np.abs(lse - rl)) <= LSE_ABS
+    assert_lse(lse, rl, decode_lse_of_rounded_query(case, cache, q_rot), name)
 
 
 def test_rope_append_bit_exact():
@@ -136,7 +98,7 @@ def test_partials_and_combine_match_oracle():
     torch.cuda.synchronize()
     ref, rl = O.combine(O.bf16_to_f64(o_bf), l_ref, case.w_uv)
     assert_close(to_f64(dc.out), ref, "combine")
-    assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
+    assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= 1e-4   # fp32 merge of exact split lse values
 
 
 @pytest.mark.parametrize("batch,ns", [(1, 16), (3, 19), (4, 64), (5, 33)])
@@ -190,7 +152,8 @@ def test_decode_many_short_sequences(st, ns):
                        case.w_uk, case.w_uv, seqs=seqs, heads=heads)
     sel = np.ix_(seqs, heads)
     assert_close(out[sel], ref[sel], "many short sequences")
-    assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
+    l16 = decode_lse_of_rounded_query(case, cache, q_rot, seqs=seqs, heads=heads)
+    assert_lse(lse[sel], rl[sel], l16[sel], "many short sequences")
 
 
 def test_paged_equals_contiguous_and_block_permutation_bitwise():
@@ -221,7 +184,7 @@ def test_split_count_invariance_and_determinism():
         ns = -(-1500 // st)
         _, out, lse = run_decode(case, st, ns, dc=dc)
         assert_close(out, ref, f"split_tokens={st}")
-        assert np.max(np.abs(lse - lse1)) <= LSE_ABS
+        assert np.max(np.abs(lse - lse1)) <= 1e-3   # same rounded query: only fp32 merge order differs
     _, a, _ = run_decode(case, 192, 8, dc=dc)
     _, b, _ = run_decode(case, 192, 8, dc=dc)
     assert np.array_equal(a, b)
@@ -259,55 +222,8 @@ def test_prefill_matches_oracle(H, lens, qlens):
     ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.cu_q_lens,
                         case.q_nope, q_rot, case.w_uk, case.w_uv)
     assert_close(to_f64(dc.out), ref, "prefill")
-    assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
-
-
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
-def test_decode_configs_full_size_sampled(cfg):
-    """The decode workloads at full size, in the planner's launch configuration; sampled (sequence, head)
-    outputs are compared with the oracle, and all outputs must be finite."""
-    say(f"[decode] config {cfg} full size")
-    case = make_config(cfg)
-    dc, out, lse = run_decode(case)
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(cfg)
-    seqs = sorted(set([0, case.batch - 1] + rng.integers(0, case.batch, 2).tolist()))
-    if cfg == 2:
-        seqs = sorted(set(seqs + [int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))]))
-    heads = sorted(set([0, case.n_heads - 1] + rng.integers(0, case.n_heads, 6).tolist()))
-    cache, q_rot = oracle_cache(case)
-    ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
-                       case.w_uk, case.w_uv, seqs=seqs, heads=heads)
-    sel = np.ix_(seqs, heads)
-    assert_close(out[sel], ref[sel], f"config {cfg} sampled")
-    assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
-
-
-def test_prefill_config4_full_size_sampled():
-    """Chunked prefill at full size (2 sequences, 1024 new tokens after 8192 cached, 128 heads): every
-    output finite; sampled (query token, head) outputs, including the first and last query of each
-    sequence, match the oracle."""
-    say("[prefill] config 4 full size")
-    case = make_config(4)
-    dc = DeviceCase(case)
-    dc.fill_history()
-    dc.append_new()
-    dc.alloc_prefill()
-    dc.prefill()
-    torch.cuda.synchronize()
-    out = to_f64(dc.out)
-    lse = dc.lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(4)
-    cu = case.cu_q_lens
-    rows = sorted(set([int(cu[0]), int(cu[1]) - 1, int(cu[1]), int(cu[2]) - 1] + rng.integers(0, int(cu[-1]), 2).tolist()))
-    heads = sorted(set([0, case.n_heads - 1] + rng.integers(0, case.n_heads, 4).tolist()))
-    cache, q_rot = oracle_cache(case)
-    ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, cu, case.q_nope, q_rot,
-                        case.w_uk, case.w_uv, rows_sel=rows, heads=heads)
-    sel = np.ix_(rows, heads)
-    assert_close(out[sel], ref[sel], "config 4 sampled")
-    assert np.max(np.abs(lse[sel] - rl[sel])) <= LSE_ABS
+    assert_lse(dc.lse.cpu().numpy().astype(np.float64), rl, prefill_lse_of_rounded_query(case, cache, q_rot),
+               "prefill")
 
 
 def test_decode_large_score_growth_uses_exact_path():
@@ -333,7 +249,7 @@ def test_decode_large_score_growth_uses_exact_path():
     ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
                        case.w_uk, case.w_uv)
     assert_close(out, ref, "growth")
-    assert np.max(np.abs(lse - rl)) <= LSE_ABS
+    assert_lse(lse, rl, decode_lse_of_rounded_query(case, cache, q_rot), "growth")
 
 
 def test_decode_absorbed_entry_point():
@@ -356,7 +272,11 @@ def test_decode_absorbed_entry_point():
     ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
                        case.w_uk, case.w_uv)
     assert_close(to_f64(dc.out), ref, "decode_absorbed")
-    assert np.max(np.abs(dc.lse.cpu().numpy() - rl)) <= LSE_ABS
+    # the same bf16 query rows fed to the fp64 attention (the entry point's own definition)
+    r16, l16 = O.decode_from_absorbed(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, q_abs,
+                                      case.w_uv, SCALE)
+    assert_close(to_f64(dc.out), r16, "decode_absorbed against its own query rows")
+    assert_lse(dc.lse.cpu().numpy().astype(np.float64), rl, l16, "decode_absorbed")
 
 
 def test_absorb_then_attend_equals_decode_bitwise():

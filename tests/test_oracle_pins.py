@@ -182,6 +182,25 @@ def pin_absorbed_equals_expanded():
     rel = np.linalg.norm(a[0] - b[0]) / np.linalg.norm(a[0])
     assert rel <= 1e-10
     assert np.allclose(a[1], b[1], rtol=0, atol=1e-10)
+    # the same attention fed the fp64 absorbed query rows directly
+    scale = O.softmax_scale(16, 8)
+    qa = O.absorb_query(P["qn"], P["qr"], P["wk"])
+    c, l, lat = O.decode_from_absorbed(P["cache"], P["table"], P["maxb"], P["lens"], qa, P["wv"], scale,
+                                       return_latent=True)
+    assert np.linalg.norm(c - a[0]) / np.linalg.norm(a[0]) <= 1e-10
+    assert np.allclose(l, a[1], rtol=0, atol=1e-10)
+    for b in range(len(P["lens"])):                        # o_lat is the softmax mean of the latents
+        rows = np.array(rows_of(P, b, int(P["lens"][b])))
+        sc = rows @ qa[b].T * scale
+        w = np.exp(sc - sc.max(axis=0))
+        assert np.allclose(lat[b], (w / w.sum(axis=0)).T @ rows[:, :64], rtol=0, atol=1e-12)
+    # causal prefill from the absorbed rows equals the expanded prefill
+    Q = tiny_problem(seed=16, H=4, d_c=64, d_r=8, d_nope=16, d_v=16, lens=(37, 20), q_lens=(9, 20), bs=16)
+    e = O.prefill(Q["cache"], Q["table"], Q["maxb"], Q["lens"], Q["cu"], Q["qn"], Q["qr"], Q["wk"], Q["wv"])
+    f_ = O.prefill_from_absorbed(Q["cache"], Q["table"], Q["maxb"], Q["lens"], Q["cu"],
+                                 O.absorb_query(Q["qn"], Q["qr"], Q["wk"]), Q["wv"], scale)
+    assert np.linalg.norm(f_[0] - e[0]) / np.linalg.norm(e[0]) <= 1e-10
+    assert np.allclose(f_[1], e[1], rtol=0, atol=1e-10)
 
 
 def pin_special_cases():
@@ -603,7 +622,27 @@ def _mut_softmax_unshifted(monkeypatch):
     monkeypatch.setattr(O, "softmax_lse", sl)
 
 
+def _mut_absorbed_prefill_sees_next_key(monkeypatch):
+    orig = O.prefill_from_absorbed
+
+    def pf(cache, table, maxb, lens, cu, q_abs, w_uv, scale, **kw):   # query at p sees keys 0 .. p + 1
+        return orig(cache, table, maxb, np.asarray(lens) + 1, cu, q_abs, w_uv, scale, **kw)
+    monkeypatch.setattr(O, "prefill_from_absorbed", pf)
+
+
+def _mut_absorbed_drops_rope(monkeypatch):
+    orig = O.decode_from_absorbed
+
+    def d(cache, table, maxb, lens, q_abs, w_uv, scale, **kw):
+        q = np.array(O._values(q_abs))
+        q[..., w_uv.shape[2]:] = 0.0
+        return orig(cache, table, maxb, lens, q, w_uv, scale, **kw)
+    monkeypatch.setattr(O, "decode_from_absorbed", d)
+
+
 MUTANTS = [
+    (_mut_absorbed_prefill_sees_next_key, [pin_absorbed_equals_expanded]),
+    (_mut_absorbed_drops_rope, [pin_absorbed_equals_expanded]),
     (_mut_lse_without_max, [pin_identical_rows]),
     (_mut_softmax_unshifted, [pin_identical_rows]),
     (_mut_fold_head_order, [pin_output_side]),
