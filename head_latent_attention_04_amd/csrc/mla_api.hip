@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <mutex>
+
 #include "../../include/mla.h"
 #include "mla_internal.h"
 
@@ -50,6 +52,33 @@ mla::CacheView view(const mla_cache* c) { return mla::CacheView{c->data, c->bloc
 int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
 
 
+// ---- the allocation-free decode's scratch --------------------------------------------------------
+// One static device array per GPU the library runs on (it lives until the process ends). Host code
+// never passes `scratch` itself to a kernel or a copy: in host code that name is a host-side
+// stand-in. Its device address is looked up once per device (with the device current) and kept.
+static __device__ __align__(256) uint8_t scratch[MLA_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+
+// Device address of the current device's scratch (hipGetSymbolAddress on the first call per device).
+hipError_t device_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_status[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_status[dev] != hipSuccess) return g_scratch_status[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 struct PrefillWorkspace {
   size_t q_abs, o_lat, lse, total;
 };
@@ -75,6 +104,8 @@ const char* mla_status_string(int status) {
     case MLA_ERR_BAD_ARG: return "MLA_ERR_BAD_ARG: a size is out of range or inconsistent";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this shape";
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: the HIP runtime rejected a launch";
+    case MLA_ERR_TOO_LARGE:
+      return "MLA_ERR_TOO_LARGE: the call needs more than the library's static scratch holds";
     default: return "unknown MLA status";
   }
 }
@@ -333,6 +364,32 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
   if (st != MLA_OK) return st;
   return mla_decode_attend(dims, cache, batch, seq_lens, workspace, workspace_bytes, split_tokens, num_splits,
                            o_partial, lse_partial, stream);
+}
+
+int mla_decode_no_alloc(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                        const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int32_t split_tokens,
+                        int32_t num_splits, uint16_t* o_partial, float* lse_partial, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if ((st = check_splits(dims, batch, split_tokens, num_splits)) != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!seq_lens || !q_nope || !q_rope || !w_uk || !o_partial || !lse_partial) return MLA_ERR_NULL;
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) || !aligned(seq_lens, 4) ||
+      !aligned(o_partial, 16) || !aligned(lse_partial, 4))
+    return MLA_ERR_BAD_ARG;
+  const size_t need = mla_decode_workspace_size(dims, batch);
+  if (need > (size_t)MLA_NO_ALLOC_SCRATCH_BYTES) return MLA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) return MLA_ERR_LAUNCH;
+  // the absorbed query rows of every head tile are written before the attention reads them (padding
+  // heads as zeros), so nothing left in the scratch by an earlier call is read
+  hipError_t e = mla::launch_absorb(batch, dims->n_heads, q_nope, q_rope, w_uk, static_cast<uint16_t*>(ws), false,
+                                    stream);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  return launched(mla::launch_attention(view(cache), batch, dims->n_heads, seq_lens, nullptr, batch,
+                                        static_cast<const uint16_t*>(ws), true, dims->scale, split_tokens, num_splits,
+                                        o_partial, lse_partial, stream));
 }
 
 int mla_decode_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,

@@ -21,7 +21,8 @@ LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_HERE, "libmla.so")
 D_C, D_ROPE, D_NOPE, D_V, BLOCK = 512, 64, 128, 128, 64
 ROW = D_C + D_ROPE
 
-MLA_OK, MLA_ERR_NULL, MLA_ERR_BAD_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH = 0, -1, -2, -3, -4
+MLA_OK, MLA_ERR_NULL, MLA_ERR_BAD_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH, MLA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+NO_ALLOC_SCRATCH_BYTES = 16 << 20
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -67,6 +68,8 @@ EXPORTS = {
     "mla_decode_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp, _i32,
                                   _i32, _vp, _sz, _vp, _vp, _vp]),
+    "mla_decode_no_alloc": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _vp,
+                                           _i32, _i32, _vp, _vp, _vp]),
     "mla_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_rope_append_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -300,6 +303,20 @@ def decode(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split
         _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
         _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
     _check("mla_decode", st)
+
+
+def decode_no_alloc(dims: MlaDims, cache: MlaCache, seq_lens, q_nope, q_rope, w_uk, split_tokens: int,
+                    num_splits: int, o_partial, lse_partial, stream=None):
+    """mla_decode without a workspace (the library's static per-GPU scratch holds the absorbed queries)."""
+    B = seq_lens.numel()
+    H = dims.n_heads
+    st = load().mla_decode_no_alloc(
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(q_nope, "q_nope", BF16, B * H * dims.d_nope), _ptr(q_rope, "q_rope", BF16, B * H * dims.d_rope),
+        _ptr(w_uk, "w_uk", BF16, H * dims.d_nope * dims.d_c), split_tokens, num_splits,
+        _ptr(o_partial, "o_partial", BF16, B * H * num_splits * dims.d_c),
+        _ptr(lse_partial, "lse_partial", F32, B * H * num_splits), _stream(stream))
+    _check("mla_decode_no_alloc", st)
 
 
 def absorb(dims: MlaDims, q_nope, q_rope, w_uk, workspace, stream=None):

@@ -56,6 +56,10 @@ extern "C" {
 #define MLA_ERR_BAD_ARG (-2)     /* a size is negative, zero where it must be positive, or inconsistent */
 #define MLA_ERR_UNSUPPORTED (-3) /* a shape this library has no kernel for */
 #define MLA_ERR_LAUNCH (-4)      /* the HIP runtime reported an error for a launch */
+#define MLA_ERR_TOO_LARGE (-5)   /* mla_decode_no_alloc: the call needs more than the static scratch holds */
+
+/* Bytes of the static device scratch of mla_decode_no_alloc (one array per GPU, kept until exit). */
+#define MLA_NO_ALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Model dimensions ("论文复现工坊 No.4", section 2: the module's constructor arguments). */
 typedef struct mla_dims {
@@ -163,6 +167,25 @@ int mla_decode(const mla_dims* dims, const mla_cache* cache, int32_t batch, cons
                const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
                int32_t split_tokens, int32_t num_splits, void* workspace, size_t workspace_bytes,
                uint16_t* o_partial, float* lse_partial, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_decode_no_alloc - mla_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. It computes exactly what
+ * mla_decode computes (same kernels, same outputs bit for bit) but takes no workspace: the absorbed
+ * queries go to a static device array of MLA_NO_ALLOC_SCRATCH_BYTES (16 MiB) that the library holds
+ * on each GPU it runs on until the process ends. Nothing is allocated and nothing is freed; the
+ * array's device address is looked up (hipGetSymbolAddress) on the first call on each device, with
+ * the call's device current (the stream must belong to the current device).
+ *   Arguments as mla_decode, without workspace / workspace_bytes.
+ *   Limit: mla_decode_workspace_size(dims, batch) <= MLA_NO_ALLOC_SCRATCH_BYTES, i.e. batch <= 113 at
+ *   n_heads = 128 (147,456 bytes per row); beyond it MLA_ERR_TOO_LARGE, before any HIP call.
+ *   All calls on one GPU share its array: calls that overlap on one GPU (different streams, or host
+ *   threads racing on one stream's enqueue order) race on it and must be serialised by the caller.
+ *   The array keeps the last call's contents; every call writes all the scratch it later reads.
+ * ------------------------------------------------------------------------------------------- */
+int mla_decode_no_alloc(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                        const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int32_t split_tokens,
+                        int32_t num_splits, uint16_t* o_partial, float* lse_partial, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_absorb / mla_decode_attend - the two halves of mla_decode, for callers that schedule or time

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.status_string(st), str)
     assert "UNSUPPORTED" in lib.status_string(-3)
 
@@ -253,3 +253,27 @@ def test_prefill_token_limit():
                                            FAKE, FAKE, FAKE, 1 << 62, FAKE, None, None)
     assert call((1 << 24) + 1) == lib.MLA_ERR_BAD_ARG
     assert lib.chunked_prefill_workspace_size(d, 70000) >= 70000 * 128 * 576 * 2
+
+
+def test_no_alloc_decode_validation():
+    """mla_decode_no_alloc takes mla_decode's arguments without a workspace; a batch whose absorbed
+    queries would not fit the static scratch is rejected before any HIP call."""
+    L = lib.load()
+    d = D()
+    c = cache()
+    na = lambda B, ptrs=(FAKE,) * 4, part=(FAKE, FAKE), st=64, ns=2: L.mla_decode_no_alloc(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(c), B, *ptrs, st, ns, *part, None)
+    per_row = lib.decode_workspace_size(d, 1)
+    assert per_row == 128 * 576 * 2
+    too_many = lib.NO_ALLOC_SCRATCH_BYTES // per_row + 1
+    assert too_many == 114
+    assert na(too_many) == lib.MLA_ERR_TOO_LARGE
+    assert "scratch" in lib.status_string(lib.MLA_ERR_TOO_LARGE)
+    assert na(2, ptrs=(FAKE, None, FAKE, FAKE)) == lib.MLA_ERR_NULL
+    assert na(2, part=(FAKE, None)) == lib.MLA_ERR_NULL
+    assert na(2, ptrs=(FAKE, MIS16, FAKE, FAKE)) == lib.MLA_ERR_BAD_ARG
+    assert na(2, part=(MIS16, FAKE)) == lib.MLA_ERR_BAD_ARG
+    assert na(2, st=100) == lib.MLA_ERR_BAD_ARG
+    assert na(0, ptrs=(None,) * 4, part=(None, None)) == lib.MLA_OK
+    assert L.mla_decode_no_alloc(ctypes.byref(D(n_heads=120)), ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, 64, 2,
+                                 FAKE, FAKE, None) == lib.MLA_ERR_UNSUPPORTED
