@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", choices=["decode", "decode_configs", "prefill", "prefill_crossover", "kv_down", "query",
-                                           "output"],
+                                           "output", "layer"],
                     default="decode",
                     help="decode: B=32, n_h=128, 4K context (the headline); decode_configs: the same decode step "
                          "on the ragged paged batch (B=64, lengths 512..32768) and on the long context (B=4, "
@@ -55,7 +55,9 @@ def parse():
                          "append of the decode step's 32 new tokens (and of the prefill chunk's 2048), width 4096; "
                          "query: the absorbed query rows of the decode step's 32 tokens straight from the hidden "
                          "state (W_UQ W_UK multiplied ahead of time), width 4096, rank 512; output: the decode "
-                         "step's output side, W_UV folded into wo against combine + wo, 32 tokens, width 4096")
+                         "step's output side, W_UV folded into wo against combine + wo, 32 tokens, width 4096; layer: one decode "
+                         "layer of the attention from the hidden state (kv_down_append, query_absorbed, attention, "
+                         "combine, wo), B=32, 4096 cached tokens, width 4096")
     return ap.parse_args()
 
 
@@ -188,6 +190,8 @@ def main():
         return query_main(args, torch, lib, props)
     if args.workload == "output":
         return output_main(args, torch, lib, props)
+    if args.workload == "layer":
+        return layer_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -823,6 +827,146 @@ def kv_down_main(args, torch, lib, props):
     }
     if not args.no_cpu:
         result["cpu_baseline"] = kv_down_cpu_baseline(dec[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def layer_bytes(B, H, L, dim, r):
+    """Algorithmic HBM bytes of one decode layer of the attention from the hidden state: the KV
+    down-projection and append, the absorbed query rows, the attention over the cache (plus its query
+    rows), the combine's W_UV and output, and wo (weight, activations, y). The split partials are an
+    intermediate of the attention and are not counted."""
+    attn = B * L * 1152 + B * H * 576 * 2
+    comb = H * 128 * 512 * 2 + B * H * 128 * 2
+    wo = dim * H * 128 * 2 + B * H * 128 * 2 + B * dim * 2
+    return kv_down_bytes(B) + query_bytes(B, H, dim, r) + attn + comb + wo
+
+
+class LayerSet:
+    """One independent copy of a decode layer's inputs, weights (prepared once) and cache."""
+
+    def __init__(self, torch, lib, case, seed):
+        from head_latent_attention_04_amd.runner import DeviceCase
+        from workloads import make_kv_down_inputs, make_output_inputs, make_query_inputs
+        B, H = case.batch, case.n_heads
+        dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to("cuda")
+        self.kin = make_kv_down_inputs(seed, B, KV_DIM)
+        self.qin = make_query_inputs(seed + 1, B, KV_DIM, H, Q_RANK)
+        self.oin = make_output_inputs(seed + 2, B, KV_DIM, H)
+        self.dc = DeviceCase(case)
+        self.dc.fill_history()
+        self.dims = self.dc.dims
+        self.pos = dev((case.seq_lens - 1).astype(np.int32), np.int32)
+        self.seq = dev(np.arange(B, dtype=np.int32), np.int32)
+        self.x = dev(self.kin.x, np.int16)
+        self.w_dkv, self.g = dev(self.kin.w_dkv, np.int16), dev(self.kin.gamma, np.int16)
+        self.w_dq, self.gq = dev(self.qin.w_dq, np.int16), dev(self.qin.gamma_q, np.int16)
+        self.w_q = torch.empty(H * 576 * Q_RANK, dtype=torch.int16, device="cuda")
+        lib.absorb_query_weights(self.dims, dev(self.qin.w_uq, np.int16), dev(self.qin.w_uk, np.int16), self.w_q)
+        self.w_o = torch.empty(KV_DIM * H * 128, dtype=torch.int16, device="cuda")
+        lib.prepare_output_weight(self.dims, dev(self.oin.w_o, np.int16), self.w_o)
+        self.ws_kv = torch.empty(lib.kv_down_append_workspace_size(self.dims, B, KV_DIM), dtype=torch.uint8,
+                                 device="cuda")
+        self.ws_q = torch.empty(lib.query_absorbed_workspace_size(self.dims, B, KV_DIM, Q_RANK), dtype=torch.uint8,
+                                device="cuda")
+        self.ws_o = torch.empty(lib.output_projection_workspace_size(self.dims, B, KV_DIM, False), dtype=torch.uint8,
+                                device="cuda")
+        self.q_abs = torch.empty((B, H, 576), dtype=torch.int16, device="cuda")
+        self.y = torch.empty((B, KV_DIM), dtype=torch.int16, device="cuda")
+        self.st, self.ns = self.dc.plan()
+        self.dc.alloc_decode(self.ns)
+
+    def kv(self, lib):
+        lib.kv_down_append(self.dims, self.dc.cache, self.seq, self.pos, self.x, self.w_dkv, self.g, KV_EPS, self.ws_kv)
+
+    def query(self, lib):
+        lib.query_absorbed(self.dims, self.pos, self.x, self.w_dq, self.gq, KV_EPS, self.w_q, self.ws_q, self.q_abs)
+
+    def attend(self, lib):
+        o, l = self.dc.partials
+        lib.decode_absorbed(self.dims, self.dc.cache, self.dc.seq_lens, self.q_abs, self.st, self.ns, o, l)
+
+    def combine(self, lib):
+        o, l = self.dc.partials
+        lib.decode_combine(self.dims, self.dc.case.batch, self.ns, o, l, self.dc.w_uv, self.dc.out, self.dc.lse)
+
+    def wo(self, lib):
+        lib.output_projection(self.dims, self.dc.out, self.w_o, KV_DIM, False, self.ws_o, self.y)
+
+    def step(self, lib):
+        self.kv(lib)
+        self.query(lib)
+        self.attend(lib)
+        self.combine(lib)
+        self.wo(lib)
+
+
+def layer_main(args, torch, lib, props):
+    """One decode layer of the attention from the hidden state (B=32, n_h=128, 4096 cached tokens, width
+    4096, q_rank 512): KV down-projection + append, absorbed query rows, attention, combine with W_UV,
+    wo. Context for the headline step, which starts from the per-head query instead."""
+    from workloads import make_config
+    case = make_config(1)
+    B, H, L = case.batch, case.n_heads, int(case.seq_lens[0])
+    sets = [LayerSet(torch, lib, case, 600 + 10 * k) for k in range(max(1, min(args.sets, 4)))]
+    torch.cuda.synchronize()
+    n = len(sets)
+    for i in range(args.warmup):
+        sets[i % n].step(lib)
+    torch.cuda.synchronize()
+    ms_step = time_loop(torch, lambda i: sets[i % n].step(lib), args.steps)
+    parts = {}
+    for name in ("kv", "query", "attend", "combine", "wo"):
+        fn = lambda i, name=name: getattr(sets[i % n], name)(lib)
+        for i in range(args.warmup):
+            fn(i)
+        parts[name] = round(time_loop(torch, fn, args.steps), 5)
+    nbytes = layer_bytes(B, H, L, KV_DIM, Q_RANK)
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "decode layer of the attention from the hidden state GB/s, n_h=128, B=32, ctx 4K, width 4096",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode layer B={B} n_h={H} ctx={L} dim={KV_DIM} q_rank={Q_RANK}: kv_down_append, "
+                               f"query_absorbed, decode_absorbed (split {sets[0].ns}x{sets[0].st}), combine, wo",
+                   "input_sets_rotated": n},
+        "kernels_ms_back_to_back": parts,
+        "launches_per_step": 9,
+        "roofline": {"kernel": "the whole layer step", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "device": props.name,
+    }
+    if not args.no_cpu:
+        from oracle import mla_oracle as O
+        s0 = sets[0]
+        from workloads import BF16_NAN
+        cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
+        cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
+                                 case.c_kv, case.k_rope)
+        wn, wr = O.q_up_split(s0.qin.w_uq, H, 128)
+        w_uqk = O.absorb_query_weights(wn, s0.qin.w_uk)
+        pos = case.seq_lens - 1
+        seq = np.arange(B)
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            c2 = O.kv_down_append(cache, case.block_table, case.max_blocks_per_seq, seq, pos, s0.kin.x, s0.kin.w_dkv,
+                                  s0.kin.gamma, KV_EPS)
+            q = O.query_absorbed(s0.kin.x, pos, s0.qin.w_dq, s0.qin.gamma_q, KV_EPS, w_uqk, wr)
+            out, _ = O.decode_from_absorbed(c2, case.block_table, case.max_blocks_per_seq, case.seq_lens, q,
+                                            case.w_uv, O.softmax_scale(128, 64))
+            O.output_projection(O.f64_to_bf16(out), s0.oin.w_o)
+            reps += 1
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+                                  "kind": "oracle", "sample": f"{reps} repetitions of the whole 32-sequence layer "
+                                                              f"chain (weights prepared outside the timing), fp64, "
+                                                              f"{dt:.1f} s"}
     print(json.dumps(result), flush=True)
 
 

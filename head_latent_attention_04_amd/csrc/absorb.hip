@@ -10,7 +10,8 @@
 //
 // Per head this is a small GEMM, computed transposed with bf16 MFMA:
 //   q_abs^T[c, r] = sum_d W_UK[h][d][c] q_nope[r, h, d]     (M = c, N = r, K = d)
-// One work-group per (head, half of the 512 latent columns, a range of 32-row blocks). The 128 x 256
+// One work-group per (head, half of the 512 latent columns, a range of 32-row blocks), ordered so that
+// the 8 heads whose pieces share an output line run on one XCD (absorb_coords). The 128 x 256
 // slice of W_UK[h] is staged in LDS once (rows padded to 544 bytes so the transposed reads of 4 rows hit
 // different banks) and read with ds_read_b64_tr_b16 as the d-contiguous A operand; q_nope rows are
 // the B operand straight from global memory. fp32 accumulation, one bf16 rounding.
@@ -154,40 +155,69 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
   }
 }
 
+// Absorption work-group a (0 <= a < 8 * n_units, in launch order) -> (head, column half, first row).
+// A unit is 8 consecutive heads with the same column half and row block: the 16-byte pieces its
+// work-groups write make up whole 128-byte lines of the operand-order output (a line holds one
+// 8-element chunk of 8 heads). Work-groups are dealt to the 8 XCDs round-robin by launch index, so
+// unit u takes the launch indices 64 (u / 8) + 8 e + u % 8 (e = 0..7, its heads): all of a unit runs
+// on one XCD, whose L2 merges the pieces into whole lines before they are written back (pieces of
+// one line from eight XCDs would be written back one by one). Units past the last multiple of 8
+// keep the plain order. (Any assignment is correct; this one is about the write traffic.)
+__device__ __forceinline__ void absorb_coords(int a, int hp, int zb, int rows_per_wg, int* h, int* ch, int* r0) {
+  const int octets = hp / 8;
+  const int n_units = octets * (kDc / kCols) * zb;
+  const int full = n_units & ~7;
+  int u, e;
+  if (a < 8 * full) {
+    u = (a & 7) + 8 * (a >> 6);
+    e = (a >> 3) & 7;
+  } else {
+    u = full + ((a - 8 * full) >> 3);
+    e = (a - 8 * full) & 7;
+  }
+  *h = 8 * (u % octets) + e;
+  *ch = (u / octets) % (kDc / kCols);
+  *r0 = (u / (octets * (kDc / kCols))) * rows_per_wg;
+}
+
 template <bool kPlain>
-__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, int rows_per_wg,
+__global__ void __launch_bounds__(256) absorb_mfma_kernel(int rows, int n_heads, int rows_per_wg, int zb,
                                                           const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           uint16_t* __restrict__ q_abs) {
   __shared__ __attribute__((aligned(16))) char w_lds[kAbsorbLds];
-  absorb_tile<kPlain>(blockIdx.x, blockIdx.y, blockIdx.z * rows_per_wg, rows, n_heads, rows_per_wg, q_nope, q_rope, w_uk,
-                      q_abs, w_lds);
+  int h, ch, r0;
+  absorb_coords(blockIdx.x, 32 * q_tiles(n_heads), zb, rows_per_wg, &h, &ch, &r0);
+  absorb_tile<kPlain>(h, ch, r0, rows, n_heads, rows_per_wg, q_nope, q_rope, w_uk, q_abs, w_lds);
 }
 
 // RoPE + append and absorption in one launch: the first n_rope work-groups are (token, head group)
 // RoPE work-groups that also write the rotated query into the RoPE part of the absorbed rows (row i
 // is token i); the rest are the absorption's (head, column half, row range) work-groups, which leave
-// that part alone. The two sets touch disjoint outputs and run side by side.
+// that part alone. The two sets touch disjoint outputs and run side by side. n_rope_slots (a multiple
+// of 8, >= n_rope) keeps the absorption's launch indices aligned to the XCD rotation; RoPE slots past
+// n_rope do nothing.
 __global__ void __launch_bounds__(256) rope_absorb_kernel(CacheView cache, int n_heads, const int32_t* __restrict__ token_seq,
                                                           const int32_t* __restrict__ token_pos,
                                                           const uint16_t* __restrict__ c_kv,
                                                           const uint16_t* __restrict__ k_rope,
                                                           uint16_t* __restrict__ q_rope, double log2_theta, int n_rope,
-                                                          int rows, int rows_per_wg, const uint16_t* __restrict__ q_nope,
+                                                          int n_rope_slots, int rows, int rows_per_wg, int zb,
+                                                          const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs) {
   __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];
   const int tiles = q_tiles(n_heads);
-  if ((int)blockIdx.x < n_rope) {
+  if ((int)blockIdx.x < n_rope_slots) {
+    if ((int)blockIdx.x >= n_rope) return;
     const int groups = rope_groups(n_heads);
     rope_token_group(cache, n_heads, blockIdx.x / groups, blockIdx.x % groups, token_seq, token_pos, c_kv, k_rope,
                      q_rope, log2_theta, q_abs, tiles, reinterpret_cast<double*>(smem));
     return;
   }
-  const int hp = 32 * tiles;
-  const int a = blockIdx.x - n_rope;
-  absorb_tile<false>(a % hp, (a / hp) % (kDc / kCols), (a / (hp * (kDc / kCols))) * rows_per_wg, rows, n_heads, rows_per_wg,
-              q_nope, nullptr, w_uk, q_abs, smem);
+  int h, ch, r0;
+  absorb_coords(blockIdx.x - n_rope_slots, 32 * tiles, zb, rows_per_wg, &h, &ch, &r0);
+  absorb_tile<false>(h, ch, r0, rows, n_heads, rows_per_wg, q_nope, nullptr, w_uk, q_abs, smem);
 }
 
 namespace {
@@ -207,13 +237,14 @@ hipError_t launch_absorb(int rows, int n_heads, const uint16_t* q_nope, const ui
   const int hp = 32 * q_tiles(n_heads);
   const int rows_per_wg = absorb_rows_per_wg(rows, n_heads);
   const int zb = (rows + rows_per_wg - 1) / rows_per_wg;
-  if (zb > 65535) return hipErrorInvalidValue;
+  const int64_t nwg = (int64_t)hp * (kDc / kCols) * zb;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (plain)
-    hipLaunchKernelGGL(absorb_mfma_kernel<true>, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads,
-                       rows_per_wg, q_nope, q_rope, w_uk, q_abs);
+    hipLaunchKernelGGL(absorb_mfma_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, stream, rows, n_heads, rows_per_wg,
+                       zb, q_nope, q_rope, w_uk, q_abs);
   else
-    hipLaunchKernelGGL(absorb_mfma_kernel<false>, dim3(hp, kDc / kCols, zb), dim3(256), 0, stream, rows, n_heads,
-                       rows_per_wg, q_nope, q_rope, w_uk, q_abs);
+    hipLaunchKernelGGL(absorb_mfma_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, stream, rows, n_heads, rows_per_wg,
+                       zb, q_nope, q_rope, w_uk, q_abs);
   return hipGetLastError();
 }
 
@@ -226,11 +257,12 @@ hipError_t launch_rope_absorb(const CacheView& cache, int n_heads, int num_token
   const int rows_per_wg = absorb_rows_per_wg(num_tokens, n_heads);
   const int64_t zb = (num_tokens + rows_per_wg - 1) / rows_per_wg;
   const int64_t n_rope = (int64_t)num_tokens * rope_groups(n_heads);
-  const int64_t total = n_rope + (int64_t)hp * (kDc / kCols) * zb;
+  const int64_t n_rope_slots = (n_rope + 7) & ~(int64_t)7;
+  const int64_t total = n_rope_slots + (int64_t)hp * (kDc / kCols) * zb;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rope_absorb_kernel, dim3((unsigned)total), dim3(256), 0, stream, cache, n_heads, token_seq, token_pos,
-                     c_kv, k_rope, q_rope, log2((double)theta), (int)n_rope, num_tokens, rows_per_wg, q_nope, w_uk,
-                     q_abs);
+                     c_kv, k_rope, q_rope, log2((double)theta), (int)n_rope, (int)n_rope_slots, num_tokens, rows_per_wg,
+                     (int)zb, q_nope, w_uk, q_abs);
   return hipGetLastError();
 }
 

@@ -290,6 +290,46 @@ int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, in
   return MLA_OK;
 }
 
+// Cost model of the two chunked-prefill forms on MI355X (rates measured with the benchmark at 2 x 1024
+// new tokens after 8192: the absorbed attention sustains 1.15 PFLOP/s, the expanded form's
+// up-projection 0.80 and its attention 0.91; the absorbed form's absorption and combine cost about
+// 0.12 us per query row; each form about 20 us of launches). The absorbed attention runs one
+// work-group per query row (per 128 heads), so fewer rows than compute units leave units idle; the
+// expanded form up-projects every cached token in 256-token tiles and attends in 256-query tiles.
+int mla_chunked_prefill_plan(const mla_dims* dims, int32_t batch, const int32_t* seq_lens, const int32_t* q_lens,
+                             int32_t num_cus, int32_t* use_expanded, float* absorbed_us, float* expanded_us) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!use_expanded) return MLA_ERR_NULL;
+  if (batch < 0 || num_cus <= 0) return MLA_ERR_BAD_ARG;
+  if (batch > 0 && (!seq_lens || !q_lens)) return MLA_ERR_NULL;
+  constexpr double kAbsorbedRate = 1.15e15, kUpRate = 0.80e15, kExpandedAttnRate = 0.91e15;
+  constexpr double kPerRowUs = 0.12, kLaunchUs = 20.0;
+  const double H = dims->n_heads;
+  auto up256 = [](double x) { return ceil(x / 256.0) * 256.0; };
+  double pairs = 0, pairs_tiles = 0, up_tokens = 0, rows = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const double L = seq_lens[b], q = q_lens[b];
+    if (q < 0 || L < 0 || q > L) return MLA_ERR_BAD_ARG;
+    if (q == 0) continue;
+    pairs += q * (L - q) + q * (q + 1) / 2;          // visible (query, key) pairs under the causal rule
+    pairs_tiles += up256(q) * (L - q) + up256(q) * up256(q) / 2;
+    up_tokens += up256(L);
+    rows += q;
+  }
+  const int groups = (mla::q_tiles(dims->n_heads) + 3) / 4;
+  const double wg = rows * groups;
+  const double wave_factor = wg > 0 ? ceil(wg / num_cus) * num_cus / wg : 1.0;
+  const double t_abs = pairs * H * 2 * (mla::kRow + mla::kDc) / kAbsorbedRate * 1e6 * wave_factor + kPerRowUs * rows +
+                       kLaunchUs;
+  const double t_exp = up_tokens * H * 2 * 256 * mla::kDc / kUpRate * 1e6 +
+                       pairs_tiles * H * 2 * (mla::kDnope + mla::kDr + mla::kDv) / kExpandedAttnRate * 1e6 + kLaunchUs;
+  *use_expanded = t_exp < t_abs ? 1 : 0;
+  if (absorbed_us) *absorbed_us = (float)t_abs;
+  if (expanded_us) *expanded_us = (float)t_exp;
+  return MLA_OK;
+}
+
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch) {
   if (check_dims(dims) != MLA_OK || batch < 0) return 0;
   return align256((size_t)batch * mla::q_tiles(dims->n_heads) * mla::kQTileElems * 2);

@@ -78,6 +78,9 @@ EXPORTS = {
     "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
                                            _i32, _vp, _vp, _vp]),
     "mla_decode_combine": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_chunked_prefill_plan": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, ctypes.POINTER(_i32),
+                                                ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32),
+                                                ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
     "mla_chunked_prefill_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32]),
     "mla_chunked_prefill": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32,
                                            _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
@@ -375,6 +378,18 @@ def decode_combine(dims: MlaDims, batch: int, num_splits: int, o_partial, lse_pa
         _ptr(w_uv, "w_uv", BF16, H * dims.d_v * dims.d_c), _ptr(out, "out", BF16, batch * H * dims.d_v),
         _ptr(lse_out, "lse_out", F32, batch * H), _stream(stream))
     _check("mla_decode_combine", st)
+
+
+def chunked_prefill_plan(dims: MlaDims, seq_lens, q_lens, num_cus: int = 256):
+    """(use_expanded, absorbed_us, expanded_us) from host sequences of cached and chunk lengths."""
+    B = len(seq_lens)
+    arr = _i32 * max(B, 1)
+    sl, ql = arr(*[int(v) for v in seq_lens]), arr(*[int(v) for v in q_lens])
+    ue, a, x = _i32(), ctypes.c_float(), ctypes.c_float()
+    _check("mla_chunked_prefill_plan", load().mla_chunked_prefill_plan(ctypes.byref(dims), B, sl, ql, num_cus,
+                                                                       ctypes.byref(ue), ctypes.byref(a),
+                                                                       ctypes.byref(x)))
+    return bool(ue.value), float(a.value), float(x.value)
 
 
 def chunked_prefill_workspace_size(dims: MlaDims, total_q: int) -> int:

@@ -249,6 +249,22 @@ int mla_decode_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, 
                        const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,
                        hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * mla_chunked_prefill_plan - which form of the causal chunked prefill is expected to be faster on
+ * MI355X (host only, no HIP call): mla_chunked_prefill (absorbed: 2 (d_c + d_rope) + 2 d_c multiply-adds
+ * per visible (query, key) pair and head) or mla_chunked_prefill_expanded (every cached token
+ * up-projected through W_UK and W_UV, then 2 (d_nope + d_rope) + 2 d_v per pair and head)
+ * ("Multi-Head Latent Attention: DeepSeek V2/V3 工程视角" names the two ways). A cost model with rates
+ * measured on MI355X; short chunks over a long prefix favour the absorbed form, long chunks the
+ * expanded one (at 8192 cached tokens the two meet at about 256 new tokens per sequence).
+ *   seq_lens, q_lens  HOST arrays [batch]: cached tokens (chunk included) and chunk lengths, 0 <= q <= L
+ *   num_cus           compute units (256 on MI355X)
+ *   use_expanded      out: 1 if the expanded form is expected faster, else 0
+ *   absorbed_us, expanded_us  out (may be NULL): the model's estimates in microseconds
+ * ------------------------------------------------------------------------------------------- */
+int mla_chunked_prefill_plan(const mla_dims* dims, int32_t batch, const int32_t* seq_lens, const int32_t* q_lens,
+                             int32_t num_cus, int32_t* use_expanded, float* absorbed_us, float* expanded_us);
+
 /* Bytes of device workspace mla_chunked_prefill needs for `total_q` query tokens. */
 size_t mla_chunked_prefill_workspace_size(const mla_dims* dims, int32_t total_q);
 

@@ -277,3 +277,27 @@ def test_no_alloc_decode_validation():
     assert na(0, ptrs=(None,) * 4, part=(None, None)) == lib.MLA_OK
     assert L.mla_decode_no_alloc(ctypes.byref(D(n_heads=120)), ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, 64, 2,
                                  FAKE, FAKE, None) == lib.MLA_ERR_UNSUPPORTED
+
+
+def test_chunked_prefill_plan_follows_the_measured_crossover():
+    """The host plan of the two prefill forms: at 8192 cached tokens the absorbed form wins for short
+    chunks, the expanded form from about 256 new tokens per sequence on (the crossover measured on
+    MI355X: 64 and 128 absorbed, 512 to 2048 expanded); a decode-like chunk of 1 token stays absorbed."""
+    d = D()
+    for q, exp in ((1, False), (64, False), (128, False), (512, True), (1024, True), (2048, True)):
+        ue, a, x = lib.chunked_prefill_plan(d, [8192 + q] * 2, [q] * 2)
+        assert ue == exp, (q, a, x)
+        assert a > 0 and x > 0
+    # estimates within 20% of the measured times at 1024 (absorbed 4.34 ms, expanded 2.29 ms)
+    _, a, x = lib.chunked_prefill_plan(d, [9216] * 2, [1024] * 2)
+    assert abs(a / 4335 - 1) < 0.2 and abs(x / 2293 - 1) < 0.2
+    # a fresh prompt (no prefix) of 4096 tokens: the expanded form does far fewer multiply-adds
+    assert lib.chunked_prefill_plan(d, [4096], [4096])[0]
+    L = lib.load()
+    import ctypes as C
+    out = C.c_int32()
+    assert L.mla_chunked_prefill_plan(C.byref(d), 1, None, None, 256, C.byref(out), None, None) == lib.MLA_ERR_NULL
+    bad = (C.c_int32 * 1)(5)
+    assert L.mla_chunked_prefill_plan(C.byref(d), 1, (C.c_int32 * 1)(4), bad, 256, C.byref(out), None, None) \
+        == lib.MLA_ERR_BAD_ARG  # chunk longer than the sequence
+    assert L.mla_chunked_prefill_plan(C.byref(d), 0, None, None, 256, C.byref(out), None, None) == lib.MLA_OK
