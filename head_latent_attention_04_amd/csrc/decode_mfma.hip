@@ -66,9 +66,29 @@ constexpr float kMaxExcess = 64.0f;                 // log2 units: softmax weigh
 __device__ __forceinline__ int rot3(int x) { return ((x & 3) << 1) | (x >> 2); }
 __device__ __forceinline__ int row_swz(int r) { return rot3(r & 7) ^ (2 * ((r >> 3) & 1)); }
 
-// P layout: head h's 32 weights at h * 64, its 8-token slot s at 16 (s ^ p_swz(h)), so that 8 or 16
-// consecutive heads reading one slot hit distinct banks.
-__device__ __forceinline__ int p_swz(int h) { return ((h >> 1) ^ (h >> 3)) & 3; }
+// P layout: head h's 32 weights at h * 64, its 8-token slot s at 16 (s ^ p_swz(h)). With this swizzle
+// both the operand reads (16 bytes per lane, lanes (h, half) reading slot 2 ksp + half) and the
+// writes (16 bytes per lane, lanes (h, half) writing slots 2 half and 2 half + 1) are free of LDS bank
+// conflicts on gfx950 (checked with the SQ_LDS_BANK_CONFLICT counter on kernels that issue exactly
+// these accesses; an earlier swizzle, ((h >> 1) ^ (h >> 3)) & 3, was 2-way conflicted on the reads).
+__device__ __forceinline__ int p_swz(int h) { return (h ^ (h >> 2)) & 3; }
+
+// Lanes l and l ^ 32 hold the low and high 8 bytes of four 16-byte chunks: x[k] (k = 0..3) the halves
+// of chunks 0 and 1 (x[0], x[1] chunk 0; x[2], x[3] chunk 1) and x[k + 4] those of chunks 2 and 3. After
+// the exchange the low lane holds whole chunks 0 (c[0]) and 1 (c[1]), the high lane whole chunks 2 and
+// 3: v_permlane32_swap hands the low lane the high lane's first operand and the high lane the low
+// lane's second operand.
+__device__ __forceinline__ void pair_chunks(const uint32_t (&x)[8], u32x4 (&c)[2]) {
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x[k], x[k + 4], false, false);
+    lo[k] = r[0];
+    hi[k] = r[1];
+  }
+  c[0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  c[1] = u32x4{lo[2], lo[3], hi[2], hi[3]};
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -411,20 +431,15 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
 
   // The loop is software-pipelined by one stage: step k scores stage k and, interleaved with those
   // MFMAs and with the softmax that follows them, reduces stage k-1 with the weights P(k-1) written
-  // at the end of step k-1 (P has two buffers, so one barrier per step suffices). Step 0 reduces a
-  // zero stage with zero weights (buffer 3 and P buffer 1 are cleared here), which adds nothing. Step k also copies stage k+2 into the buffer of stage k-2,
-  // one instruction every fourth score MFMA, so no wave stalls on a burst of copy instructions.
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < kPBytes / 16; i += kWaves * 64)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(pl + kPBytes + 16 * i) = z;
-    for (int i = threadIdx.x; i < kStageBytes / 16; i += kWaves * 64)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + (kStages - 1) * kStageBytes + 16 * i) = z;
-  }
+  // at the end of step k-1 (P has two buffers, so one barrier per step suffices). Step 0 has no
+  // previous stage and runs a copy of the body without the reduction (kReduce false). Step k also
+  // copies stage k+2 into the buffer of stage k-2, one instruction every fourth score MFMA, so no
+  // wave stalls on a burst of copy instructions.
   constexpr int kScorePv = 4 * HT;            // reduction MFMAs interleaved with the scores
   constexpr int kSoftPv = 8 * HT - kScorePv;  // the rest, spread over the softmax
   uint32_t pw[8];
-  for (int k = 0; k < nstages; ++k) {
+  auto step = [&](const int k, auto REDUCE) {
+    constexpr bool kReduce = decltype(REDUCE)::value;
     // stage k has landed once only the stage issued after it (if any) is outstanding
     if (k + 1 < nstages)
       wait_vmcnt<kBands>();
@@ -443,7 +458,7 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
 
     // every wave runs this body; a wave without a head tile scores a duplicate and drops it
     const int valid = min(kStageTok, t1 - t0 - k * kStageTok);
-    pv_begin(stp, pp);
+    if constexpr (kReduce) pv_begin(stp, pp);
     // ---- scores S^T[32 tokens x 32 heads]; half of stage k-1's reduction and the copy interleaved
     f32x16 sacc;
     {
@@ -460,7 +475,8 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
           score_mfma_first(sacc, a, qreg[0]);
         else
           score_mfma(sacc, a, qreg[ks]);
-        static_for<ks * kScorePv / 36, (ks + 1) * kScorePv / 36>([&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
+        if constexpr (kReduce)
+          static_for<ks * kScorePv / 36, (ks + 1) * kScorePv / 36>([&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
         if constexpr ((ks & 3) == 1) {
           if (copy_next) stage_copy_band(cp, ks >> 2);
         }
@@ -473,8 +489,9 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
     // of stage k-1's reduction runs on the matrix cores meanwhile (12 slots).
     auto pv_slot = [&](auto SLOT) {
       constexpr int slot = decltype(SLOT)::value;
-      static_for<kScorePv + slot * kSoftPv / 12, kScorePv + (slot + 1) * kSoftPv / 12>(
-          [&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
+      if constexpr (kReduce)
+        static_for<kScorePv + slot * kSoftPv / 12, kScorePv + (slot + 1) * kSoftPv / 12>(
+            [&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
       __builtin_amdgcn_sched_barrier(0);
     };
     using S0 = std::integral_constant<int, 0>;
@@ -508,15 +525,21 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
       pv_slot(std::integral_constant<int, 3 + (j >> 1)>{});
     });
     pv_slot(S11{});
-    if (qk_wave) {  // P(k)[head][tokens 8 q + 4 kh .. +3] <- (pw[2q], pw[2q+1]), into the other buffer
+    if (qk_wave) {  // P(k)[head][tokens 8 q .. 8 q + 7] into the other buffer, whole 16-byte slots:
+      // the lane holds tokens 8 q + 4 kh .. +3 as (pw[2q], pw[2q+1]); after the pair exchange lane kh
+      // writes slots 2 kh and 2 kh + 1
+      u32x4 chunk[2];
+      pair_chunks(pw, chunk);
       const int ps = p_swz(n);
       lds_char* pk = pl + (k & 1) * kPBytes;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(pk + hl * kPHeadBytes + 16 * (q ^ ps) + 8 * kh) =
-            u32x2{pw[2 * q], pw[2 * q + 1]};
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(pk + hl * kPHeadBytes + 16 * ((2 * kh + t) ^ ps)) =
+            chunk[t];
     }
-  }
+  };
+  step(0, std::false_type{});
+  for (int k = 1; k < nstages; ++k) step(k, std::true_type{});
   wg_barrier();  // publishes P of the last stage
   pv_all(lds + ((nstages - 1) % kStages) * kStageBytes, pl + ((nstages - 1) & 1) * kPBytes);
   wg_barrier();  // every wave is done with the stages and P
@@ -538,21 +561,27 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
   wg_barrier();  // publishes 1/lsum of every head
 
   // Scale by 1/lsum and stage as bf16 rows: element j of o[dt * HT + ht] is head 32 ht + n, latent
-  // column 128 wave + 32 dt + 8 (j >> 2) + 4 kh + (j & 3).
+  // column 128 wave + 32 dt + 8 (j >> 2) + 4 kh + (j & 3). The lane pair (l, l ^ 32) trades halves so
+  // that every store is a whole 16-byte piece of 8 columns (the 8-byte stores of the halves were 2-way
+  // bank conflicted at this pitch; the 16-byte ones are not).
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const float iv = inv_lds[32 * ht + n];
-    char* orow = smem_raw + (32 * ht + n) * kOutPitch + 2 * (128 * wave + 4 * kh);
+    char* orow = smem_raw + (32 * ht + n) * kOutPitch + 2 * (128 * wave);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
+      uint32_t w[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x2 v01 = {o[dt * HT + ht][4 * q] * iv, o[dt * HT + ht][4 * q + 1] * iv};
         const f32x2 v23 = {o[dt * HT + ht][4 * q + 2] * iv, o[dt * HT + ht][4 * q + 3] * iv};
-        *reinterpret_cast<uint2*>(orow + 2 * (32 * dt + 8 * q)) =
-            make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2)),
-                       __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2)));
+        w[2 * q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+        w[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
       }
+      u32x4 chunk[2];
+      pair_chunks(w, chunk);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) *reinterpret_cast<u32x4*>(orow + 2 * (32 * dt + 8 * (2 * kh + t))) = chunk[t];
     }
   }
   wg_barrier();
