@@ -123,33 +123,66 @@ def time_percentiles(torch, fn, n):
     return [round(t[min(n - 1, int(q * n))], 5) for q in (0.1, 0.5, 0.9)]
 
 
+def host_info():
+    """The host the CPU baseline ran on: worker threads, CPU model, BLAS library."""
+    info = {"threads": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            b = blas[0]
+            info["threads"] = int(b.get("num_threads", info["threads"]))
+            info["blas"] = f"{b.get('internal_api')} {b.get('version')} ({b.get('architecture')} kernels, " \
+                           f"{b.get('threading_layer')})"
+    except Exception:  # pragma: no cover
+        pass
+    return info
+
+
 def cpu_baseline(case, budget_s):
     """fp64 expanded-form oracle on whole sequences (all heads) of the same workload, until the
-    time budget is spent; rate in the metric's unit (algorithmic TFLOP/s of absorbed decode)."""
+    time budget is spent; rate in the metric's unit (algorithmic TFLOP/s of absorbed decode). Beside
+    it, the fp64 absorbed form (the oracle's decode_absorbed) on the same sequences for a third of the
+    budget: the same result from about 1/120 of the multiply-adds per cached token and head
+    (2 (576 + 512) against the expanded form's 2 (2 x 128 x 512) for the keys and values plus 2 (192 + 128))."""
     import numpy as np
 
     from oracle import mla_oracle as O
     from workloads import BF16_NAN
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    info = host_info()
     cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
     cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
                              case.c_kv, case.k_rope)
     q_rot = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(case.q_rope), case.q_positions()[:, None]))
-    done, flops = 0, 0.0
-    t0 = time.perf_counter()
-    while done < case.batch and time.perf_counter() - t0 < budget_s:
-        O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot, case.w_uk,
-                 case.w_uv, seqs=[done])
-        flops += step_flops_one_seq(case, done)
-        done += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {case.batch} sequences (all {case.n_heads} heads, L={int(case.seq_lens[0])}), "
-                      f"fp64 expanded form, {dt:.1f} s"}
+    args = (cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot, case.w_uk, case.w_uv)
+
+    def timed(fn, budget):
+        done, flops = 0, 0.0
+        t0 = time.perf_counter()
+        while done < case.batch and (done == 0 or time.perf_counter() - t0 < budget):
+            fn(*args, seqs=[done])
+            flops += step_flops_one_seq(case, done)
+            done += 1
+        return done, flops, time.perf_counter() - t0
+
+    done, flops, dt = timed(O.decode, budget_s)
+    done_a, flops_a, dt_a = timed(O.decode_absorbed, budget_s / 3)
+    L = int(case.seq_lens[0])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(info["threads"]), "kind": "oracle",
+            "sample": f"{done} of {case.batch} sequences (all {case.n_heads} heads, L={L}), fp64 expanded form, "
+                      f"{dt:.1f} s",
+            "cpu_model": info["cpu_model"], "blas": info["blas"],
+            "absorbed_form": {"value": round(flops_a / dt_a / 1e12, 6), "unit": "TFLOP/s",
+                              "sample": f"{done_a} of {case.batch} sequences, fp64 absorbed form (the oracle's "
+                                        f"decode_absorbed), {dt_a:.1f} s"}}
 
 
 def step_flops_one_seq(case, b):
@@ -356,11 +389,8 @@ def prefill_cpu_baseline(case, budget_s):
     is spent; rate in algorithmic TFLOP/s."""
     from oracle import mla_oracle as O
     from workloads import BF16_NAN
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    info = host_info()
+    threads = info['threads']
     cache = np.full((case.num_blocks, 64, 576), BF16_NAN, np.uint16)
     cache, _ = O.rope_append(cache, case.block_table, case.max_blocks_per_seq, case.token_seq, case.token_pos,
                              case.c_kv, case.k_rope)
@@ -378,6 +408,7 @@ def prefill_cpu_baseline(case, budget_s):
         j += 97  # spread the sample over both sequences and all positions
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                                  "cpu_model": info["cpu_model"], "blas": info["blas"],
             "sample": f"{len(rows)} of {len(pos_all)} query tokens (every 97th, all {H} heads), fp64 expanded "
                       f"form, {dt:.1f} s"}
 
@@ -542,8 +573,13 @@ def crossover_main(args, torch, lib, props):
         n = max(3, min(args.steps, 10))
         ms_a = time_each(torch, lambda i: dc.prefill(), n)
         ms_x = time_each(torch, lambda i: dc.prefill_expanded(), n)
+        use_x, est_a, est_x = lib.chunked_prefill_plan(dc.dims, [prefix + q] * 2, [q] * 2,
+                                                        props.multi_processor_count)
         rows.append({"q_per_seq": q, "absorbed_ms": round(ms_a, 4), "expanded_ms": round(ms_x, 4),
-                     "expanded_speedup": round(ms_a / ms_x, 3)})
+                     "expanded_speedup": round(ms_a / ms_x, 3),
+                     "plan": {"form": "expanded" if use_x else "absorbed", "absorbed_ms_est": round(est_a / 1e3, 4),
+                              "expanded_ms_est": round(est_x / 1e3, 4),
+                              "picked_the_faster": bool(use_x) == bool(ms_x < ms_a)}})
         if crossover is None and ms_x < ms_a:
             crossover = q
         del dc
@@ -638,14 +674,12 @@ def output_main(args, torch, lib, props):
             O.output_folded(inp.o_lat, w_ov)
             reps += 1
         dt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = len(os.sched_getaffinity(0))
+        info = host_info()
+        threads = info['threads']
         sample_bytes = 64 * H * 512 * 2 + T * H * 512 * 2 + T * 64 * 2
         result["cpu_baseline"] = {"value": round(reps * sample_bytes / dt / 1e9, 4), "unit": "GB/s",
                                   "cores": int(threads), "kind": "oracle",
+                                  "cpu_model": info["cpu_model"], "blas": info["blas"],
                                   "sample": f"{reps} repetitions of the folded projection onto 64 of the {dim} "
                                             f"output columns (the weight folded outside the timing), fp64, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -717,13 +751,11 @@ def query_main(args, torch, lib, props):
             O.query_absorbed(inp.x, np.full(T, 4095), inp.w_dq, inp.gamma_q, KV_EPS, w_uqk, wr)
             reps += 1
         dt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = len(os.sched_getaffinity(0))
+        info = host_info()
+        threads = info['threads']
         result["cpu_baseline"] = {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-                                  "kind": "oracle", "sample": f"{reps} repetitions of the whole 32-token call "
+                                  "kind": "oracle", "cpu_model": info["cpu_model"], "blas": info["blas"],
+                                  "sample": f"{reps} repetitions of the whole 32-token call "
                                                               f"(weights prepared outside the timing), fp64, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
 
@@ -756,11 +788,8 @@ def kv_down_cpu_baseline(kset, budget_s):
     spent; rate in the metric's unit (GB/s of algorithmic bytes)."""
     from oracle import mla_oracle as O
     from workloads import BF16_NAN
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    info = host_info()
+    threads = info['threads']
     ts, tp, table, nb, mb, inp = kset.host
     reps = 0
     t0 = time.perf_counter()
@@ -770,8 +799,8 @@ def kv_down_cpu_baseline(kset, budget_s):
         reps += 1
     dt = time.perf_counter() - t0
     return {"value": round(reps * kv_down_bytes(kset.T) / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "sample": f"{reps} repetitions of the whole {kset.T}-token append, width {KV_DIM}, "
-                                        f"fp64, {dt:.1f} s"}
+            "kind": "oracle", "cpu_model": info["cpu_model"], "blas": info["blas"],
+            "sample": f"{reps} repetitions of the whole {kset.T}-token append, width {KV_DIM}, fp64, {dt:.1f} s"}
 
 
 def kv_down_bytes(T):
@@ -958,13 +987,11 @@ def layer_main(args, torch, lib, props):
             O.output_projection(O.f64_to_bf16(out), s0.oin.w_o)
             reps += 1
         dt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = len(os.sched_getaffinity(0))
+        info = host_info()
+        threads = info['threads']
         result["cpu_baseline"] = {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-                                  "kind": "oracle", "sample": f"{reps} repetitions of the whole 32-sequence layer "
+                                  "kind": "oracle", "cpu_model": info["cpu_model"], "blas": info["blas"],
+                                  "sample": f"{reps} repetitions of the whole 32-sequence layer "
                                                               f"chain (weights prepared outside the timing), fp64, "
                                                               f"{dt:.1f} s"}
     print(json.dumps(result), flush=True)
