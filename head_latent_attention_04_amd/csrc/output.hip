@@ -15,9 +15,9 @@
 //   * fold_output_weights_kernel: W_OV in fp32 outer products over the 128 value rows of each head,
 //     written in operand order.
 //   * oo_splitk_gemm_kernel + reduce_bf16_kernel: y = act W^T for few rows and a long K (n_heads x
-//     128 or n_heads x 512): work-group (32 output columns, split of K, 32 rows), four waves on
-//     quarters of the split; the weight loads are contiguous 1 KB, the activations (small, cached)
-//     are loaded row by row; fp32 partials per split, then one pass adds them and rounds.
+//     128 or n_heads x 512): work-group (split of K, four 32-column tiles, 32 rows); the split's
+//     activations are staged in LDS once and each wave streams one tile's weight as contiguous 1 KB
+//     operand loads; fp32 partials per split, then one pass adds them and rounds.
 #include <algorithm>
 
 #include "mla_internal.h"
@@ -29,18 +29,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kOutMaxSplits = 64;
+constexpr int kOoChunk = 1024;               // K columns of activations per LDS fill
+constexpr int kOoPitch = kOoChunk * 2 + 16;  // LDS row pitch (bytes): rows 4 banks apart
 
 __host__ __device__ inline int64_t oo_offset(int n, int64_t k, int64_t K) {
   return (((int64_t)(n / 32) * (K / 16) + k / 16) * 64 + n % 32 + 32 * ((k / 8) & 1)) * 8 + k % 8;
 }
 
-int oo_splits(int M, int N, int64_t K) {
-  // 32-column tiles x splits x row blocks: about 2048 work-groups, each wave 16 K steps or more
-  const int tiles = (N / 32) * ((M + 31) / 32);
-  int ns = (int)std::min<int64_t>(K / 1024, std::max(1, 2048 / std::max(1, tiles)));
-  ns = std::max(1, std::min(ns, kOutMaxSplits));
-  while ((K / 64) % ns != 0) --ns;
-  return ns;
+struct OoSplit {
+  int count;          // splits of K (one fp32 partial each)
+  int64_t split_len;  // K columns per split, a multiple of kOoChunk
+};
+
+OoSplit oo_split(int M, int N, int64_t K) {
+  // about 512 work-groups (two per compute unit), each split a whole number of LDS chunks
+  const int64_t groups = (int64_t)((N / 32 + 3) / 4) * ((M + 31) / 32);
+  const int64_t chunks = (K + kOoChunk - 1) / kOoChunk;
+  int64_t per = std::max<int64_t>(1, (chunks * groups) / 512);
+  per = std::max<int64_t>(per, (chunks + kOutMaxSplits - 1) / kOutMaxSplits);
+  return OoSplit{(int)((chunks + per - 1) / per), per * kOoChunk};
 }
 }  // namespace
 
@@ -138,45 +145,63 @@ __global__ void __launch_bounds__(256) fold_output_weights_kernel(int dim, int n
 }
 
 // ---- y = act W^T, split over K -------------------------------------------------------------------
+// Work-group (split s, column group cg of 4 tiles, row block tb): the activations of rows
+// 32 tb .. +31 over the split's K range are copied into LDS once, in chunks of kOoChunk columns; wave w
+// then streams the operand-order weight of column tile 4 cg + w over the chunk (one contiguous 1 KB per
+// K step, eight loads in flight) against LDS reads of the activations, and accumulates the whole split
+// in one 32 x 32 fp32 tile. The weight is read exactly once; the activations (a few MB at most) come
+// from L2 once per column group.
 __global__ void __launch_bounds__(256) oo_splitk_gemm_kernel(int M, int N, int64_t K, int64_t split_len,
                                                              const uint16_t* __restrict__ act,
                                                              const uint16_t* __restrict__ w_op,
                                                              float* __restrict__ part) {
-  __shared__ float red[4 * 32 * 32];
-  const int ct = blockIdx.x, s = blockIdx.y, tb = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t quarter = split_len / 4;
-  const int64_t k0 = s * split_len + wave * quarter;
-  const int steps = (int)(quarter / 16);
-  const int row = min(32 * tb + (lane & 31), M - 1);
-  const uint16_t* pa = act + (int64_t)row * K + k0 + 8 * (lane >> 5);
-  const uint16_t* pb = w_op + ((int64_t)ct * (K / 16) + k0 / 16) * 512 + lane * 8;
+  __shared__ __attribute__((aligned(16))) char sa[32 * kOoPitch];
+  const int s = blockIdx.x, cg = blockIdx.y, tb = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ct = 4 * cg + wave;
+  const bool active = ct < N / 32;  // the last group may hold fewer than four tiles
+  const int64_t kbeg = (int64_t)s * split_len, kend = std::min<int64_t>(K, kbeg + split_len);
+  const uint16_t* pb = w_op + ((int64_t)(active ? ct : 0) * (K / 16)) * 512 + lane * 8;
+  const char* arow = sa + (lane & 31) * kOoPitch + 16 * (lane >> 5);
   f32x16 acc = f32x16{};
-  for (int k = 0; k < steps; k += 8) {
-    bf16x8 a[8], b[8];
+  for (int64_t k0 = kbeg; k0 < kend; k0 += kOoChunk) {
+    const int klen = (int)std::min<int64_t>(kOoChunk, kend - k0);  // a multiple of 16
+    if (k0 != kbeg) __syncthreads();                              // the previous chunk is consumed
+    for (int i = tid; i < 32 * (klen / 8); i += 256) {
+      const int r = i / (klen / 8), c = i % (klen / 8);
+      const int row = std::min(32 * tb + r, M - 1);
+      *reinterpret_cast<uint4*>(sa + r * kOoPitch + 16 * c) =
+          *reinterpret_cast<const uint4*>(act + (int64_t)row * K + k0 + 8 * c);
+    }
+    __syncthreads();
+    if (active) {
+      const uint16_t* pk = pb + (k0 / 16) * 512;
+      const int steps = klen / 16;
+      int k = 0;
+      for (; k + 8 <= steps; k += 8) {
+        bf16x8 b[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (k + u < steps) {
-        a[u] = *reinterpret_cast<const bf16x8*>(pa + (int64_t)(k + u) * 16);
-        b[u] = *reinterpret_cast<const bf16x8*>(pb + (int64_t)(k + u) * 512);
+        for (int u = 0; u < 8; ++u) b[u] = *reinterpret_cast<const bf16x8*>(pk + (int64_t)(k + u) * 512);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * (k + u));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[u], acc, 0, 0, 0);
+        }
+      }
+      for (; k < steps; ++k) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(pk + (int64_t)k * 512);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (k + u < steps) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], acc, 0, 0, 0);
   }
+  if (!active) return;
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
   // D: lane holds row 8 (e / 4) + 4 (lane / 32) + e % 4 and column lane % 32 of the tile
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-    red[(wave * 32 + m) * 32 + (lane & 31)] = acc[e];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-    const int m = e >> 5, n = e & 31;
-    const int t = 32 * tb + m;
-    if (t < M) part[((int64_t)s * M + t) * N + 32 * ct + n] = red[e] + red[1024 + e] + red[2048 + e] + red[3072 + e];
+    const int t = 32 * tb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    if (t < M) part[((int64_t)s * M + t) * N + 32 * ct + (lane & 31)] = acc[e];
   }
 }
 
@@ -229,18 +254,19 @@ hipError_t launch_fold_output_weights(int dim, int n_heads, const uint16_t* w_o,
   return hipGetLastError();
 }
 
-size_t output_workspace_bytes(int M, int N, int64_t K) { return (size_t)oo_splits(M, N, K) * M * N * 4; }
+size_t output_workspace_bytes(int M, int N, int64_t K) { return (size_t)oo_split(M, N, K).count * M * N * 4; }
 
 hipError_t launch_output_gemm(int M, int N, int64_t K, const uint16_t* act, const uint16_t* w_op, void* workspace,
                               uint16_t* y, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   if (N % 32 != 0 || K % 64 != 0) return hipErrorInvalidValue;
-  const int ns = oo_splits(M, N, K);
-  const int tblocks = (M + 31) / 32;
-  if (tblocks > 65535) return hipErrorInvalidValue;
+  const OoSplit sp = oo_split(M, N, K);
+  const int ns = sp.count;
+  const int tblocks = (M + 31) / 32, groups = (N / 32 + 3) / 4;
+  if (tblocks > 65535 || groups > 65535) return hipErrorInvalidValue;
   float* part = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(oo_splitk_gemm_kernel, dim3(N / 32, ns, tblocks), dim3(256), 0, stream, M, N, K, K / ns, act, w_op,
-                     part);
+  hipLaunchKernelGGL(oo_splitk_gemm_kernel, dim3(ns, groups, tblocks), dim3(256), 0, stream, M, N, K, sp.split_len, act,
+                     w_op, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t count4 = (int64_t)M * N / 4;
