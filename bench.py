@@ -56,8 +56,9 @@ def parse():
                          "query: the absorbed query rows of the decode step's 32 tokens straight from the hidden "
                          "state (W_UQ W_UK multiplied ahead of time), width 4096, rank 512; output: the decode "
                          "step's output side, W_UV folded into wo against combine + wo, 32 tokens, width 4096; layer: one decode "
-                         "layer of the attention from the hidden state (kv_down_append, query_absorbed, attention, "
-                         "combine, wo), B=32, 4096 cached tokens, width 4096")
+                         "layer of the attention from the hidden state (kv_down_query_absorbed, attention, combine, wo; "
+                         "the separate kv_down_append + query_absorbed calls timed beside), B=32, 4096 cached tokens, "
+                         "width 4096")
     return ap.parse_args()
 
 
@@ -897,6 +898,8 @@ class LayerSet:
                                  device="cuda")
         self.ws_q = torch.empty(lib.query_absorbed_workspace_size(self.dims, B, KV_DIM, Q_RANK), dtype=torch.uint8,
                                 device="cuda")
+        self.ws_kq = torch.empty(lib.kv_down_query_absorbed_workspace_size(self.dims, B, KV_DIM, Q_RANK),
+                                 dtype=torch.uint8, device="cuda")
         self.ws_o = torch.empty(lib.output_projection_workspace_size(self.dims, B, KV_DIM, False), dtype=torch.uint8,
                                 device="cuda")
         self.q_abs = torch.empty((B, H, 576), dtype=torch.int16, device="cuda")
@@ -910,6 +913,10 @@ class LayerSet:
     def query(self, lib):
         lib.query_absorbed(self.dims, self.pos, self.x, self.w_dq, self.gq, KV_EPS, self.w_q, self.ws_q, self.q_abs)
 
+    def kv_query(self, lib):
+        lib.kv_down_query_absorbed(self.dims, self.dc.cache, self.seq, self.pos, self.x, self.w_dkv, self.g, KV_EPS,
+                                   self.w_dq, self.gq, KV_EPS, self.w_q, self.ws_kq, self.q_abs)
+
     def attend(self, lib):
         o, l = self.dc.partials
         lib.decode_absorbed(self.dims, self.dc.cache, self.dc.seq_lens, self.q_abs, self.st, self.ns, o, l)
@@ -922,6 +929,12 @@ class LayerSet:
         lib.output_projection(self.dims, self.dc.out, self.w_o, KV_DIM, False, self.ws_o, self.y)
 
     def step(self, lib):
+        self.kv_query(lib)
+        self.attend(lib)
+        self.combine(lib)
+        self.wo(lib)
+
+    def step_separate(self, lib):
         self.kv(lib)
         self.query(lib)
         self.attend(lib)
@@ -943,8 +956,9 @@ def layer_main(args, torch, lib, props):
         sets[i % n].step(lib)
     torch.cuda.synchronize()
     ms_step = time_loop(torch, lambda i: sets[i % n].step(lib), args.steps)
+    ms_step_sep = time_loop(torch, lambda i: sets[i % n].step_separate(lib), args.steps)
     parts = {}
-    for name in ("kv", "query", "attend", "combine", "wo"):
+    for name in ("kv_query", "kv", "query", "attend", "combine", "wo"):
         fn = lambda i, name=name: getattr(sets[i % n], name)(lib)
         for i in range(args.warmup):
             fn(i)
@@ -956,11 +970,12 @@ def layer_main(args, torch, lib, props):
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"decode layer B={B} n_h={H} ctx={L} dim={KV_DIM} q_rank={Q_RANK}: kv_down_append, "
-                               f"query_absorbed, decode_absorbed (split {sets[0].ns}x{sets[0].st}), combine, wo",
+        "config": {"workload": f"decode layer B={B} n_h={H} ctx={L} dim={KV_DIM} q_rank={Q_RANK}: "
+                               f"kv_down_query_absorbed, decode_absorbed (split {sets[0].ns}x{sets[0].st}), combine, wo",
                    "input_sets_rotated": n},
         "kernels_ms_back_to_back": parts,
-        "launches_per_step": 9,
+        "launches_per_step": 7,
+        "ms_per_step_separate_kv_and_query_calls": round(ms_step_sep, 5),
         "roofline": {"kernel": "the whole layer step", "bound": "hbm", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes},

@@ -234,13 +234,15 @@ __global__ void __launch_bounds__(256) gemm_bt_partial_kernel(int M, int N, int 
 // Work-group (column tile of 32, split s, block of 32 rows): wave w takes a quarter of the split's K
 // range with v_mfma_f32_32x32x16_bf16 straight from global memory (both operands K-contiguous), two
 // K steps of operands in flight; the four partial tiles are added through LDS. Many splits spread
-// the weight B over many work-groups, so it streams from HBM once at full width.
+// the weight B over many work-groups, so it streams from HBM once at full width. B may be two weights
+// over the same K stacked by rows: columns n < N1 are rows of B, the rest rows n - N1 of B2.
 constexpr int kKStep = 16;  // K per MFMA
 constexpr int kAhead = 4;   // K steps whose operands are loaded ahead (a 64-long quarter at once)
 
 __global__ void __launch_bounds__(256) splitk_gemm_kernel(int M, int N, int K, int split_len,
                                                           const uint16_t* __restrict__ A,
-                                                          const uint16_t* __restrict__ B,
+                                                          const uint16_t* __restrict__ B, int N1,
+                                                          const uint16_t* __restrict__ B2,
                                                           float* __restrict__ part) {
   __shared__ float red[4 * 32 * 32];
   const int ct = blockIdx.x, s = blockIdx.y, tb = blockIdx.z;
@@ -251,8 +253,10 @@ __global__ void __launch_bounds__(256) splitk_gemm_kernel(int M, int N, int K, i
   // A: row 32 tb + lane % 32 (clamped; rows past the end are computed and not stored), K half lane / 32
   const int row = min(32 * tb + (lane & 31), M - 1);
   const uint16_t* pa = A + (int64_t)row * K + k0 + 8 * (lane >> 5);
-  // B: output column 32 ct + lane % 32, the same K half
-  const uint16_t* pb = B + (int64_t)(32 * ct + (lane & 31)) * K + k0 + 8 * (lane >> 5);
+  // B: output column 32 ct + lane % 32 (a row of B, or of B2 past N1; N1 is a multiple of 32), the
+  // same K half
+  const int col = 32 * ct + (lane & 31);
+  const uint16_t* pb = (32 * ct < N1 ? B + (int64_t)col * K : B2 + (int64_t)(col - N1) * K) + k0 + 8 * (lane >> 5);
   bf16x8 a[kAhead], b[kAhead];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) {
@@ -299,14 +303,22 @@ int splitk_splits(int M, int N, int K) {
   return ns;
 }
 
-hipError_t launch_splitk_gemm(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
-                              hipStream_t stream) {
-  if (M <= 0 || N % 32 != 0 || K % 64 != 0 || nsplit < 1 || (K / 64) % nsplit != 0) return hipErrorInvalidValue;
+hipError_t launch_splitk_gemm2(int M, int N1, int N2, int K, int nsplit, const uint16_t* A, const uint16_t* B,
+                               const uint16_t* B2, float* part, hipStream_t stream) {
+  const int N = N1 + N2;
+  if (M <= 0 || N1 % 32 != 0 || N2 % 32 != 0 || N <= 0 || K % 64 != 0 || nsplit < 1 || (K / 64) % nsplit != 0 ||
+      (N2 > 0 && B2 == nullptr))
+    return hipErrorInvalidValue;
   const int tblocks = (M + 31) / 32;
   if (tblocks > 65535 || nsplit > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(splitk_gemm_kernel, dim3(N / 32, nsplit, tblocks), dim3(256), 0, stream, M, N, K, K / nsplit, A, B,
-                     part);
+                     N1, B2, part);
   return hipGetLastError();
+}
+
+hipError_t launch_splitk_gemm(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
+                              hipStream_t stream) {
+  return launch_splitk_gemm2(M, N, 0, K, nsplit, A, B, nullptr, part, stream);
 }
 
 int gemm_bt_splits(int M, int N, int K) {

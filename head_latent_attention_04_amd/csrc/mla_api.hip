@@ -269,6 +269,37 @@ int mla_kv_down_append(const mla_dims* dims, const mla_cache* cache, int32_t num
                                       dims->rope_theta, workspace, stream));
 }
 
+size_t mla_kv_down_query_absorbed_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim,
+                                                 int32_t q_rank) {
+  if (check_dims(dims) != MLA_OK || num_tokens < 0 || num_tokens > 65535 * 32 || dim <= 0 || dim % 64 != 0 ||
+      q_rank <= 0 || q_rank % 64 != 0 || q_rank > 2048)
+    return 0;
+  return mla::kv_down_query_workspace_bytes(num_tokens, dim, q_rank);
+}
+
+int mla_kv_down_query_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens,
+                               const int32_t* token_seq, const int32_t* token_pos, const uint16_t* x, int32_t dim,
+                               const uint16_t* w_dkv, const uint16_t* gamma_kv, float eps_kv, const uint16_t* w_dq,
+                               const uint16_t* gamma_q, float eps_q, int32_t q_rank, const uint16_t* w_q,
+                               void* workspace, size_t workspace_bytes, uint16_t* q_abs, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535 * 32 || dim <= 0 || q_rank <= 0) return MLA_ERR_BAD_ARG;
+  if (!(eps_kv >= 0.f) || !isfinite(eps_kv) || !(eps_q >= 0.f) || !isfinite(eps_q)) return MLA_ERR_BAD_ARG;
+  if (dim % 64 != 0 || q_rank % 64 != 0 || q_rank > 2048) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MLA_OK;
+  if (!token_seq || !token_pos || !x || !w_dkv || !gamma_kv || !w_dq || !gamma_q || !w_q || !workspace || !q_abs)
+    return MLA_ERR_NULL;
+  if (workspace_bytes < mla::kv_down_query_workspace_bytes(num_tokens, dim, q_rank)) return MLA_ERR_BAD_ARG;
+  if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(w_dkv, 16) || !aligned(w_dq, 16) ||
+      !aligned(w_q, 16) || !aligned(q_abs, 8))
+    return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_kv_down_query(view(cache), dims->n_heads, num_tokens, token_seq, token_pos, x, dim,
+                                            w_dkv, gamma_kv, eps_kv, w_dq, gamma_q, eps_q, q_rank, w_q,
+                                            dims->rope_theta, workspace, q_abs, stream));
+}
+
 int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, int32_t num_cus,
                     int32_t* split_tokens, int32_t* num_splits) {
   int st = check_dims(dims);

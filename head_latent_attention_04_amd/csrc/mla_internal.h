@@ -109,6 +109,10 @@ hipError_t launch_gemm_bt_partial(int M, int N, int K, int nsplit, const uint16_
 int splitk_splits(int M, int N, int K);
 hipError_t launch_splitk_gemm(int M, int N, int K, int nsplit, const uint16_t* A, const uint16_t* B, float* part,
                               hipStream_t stream);
+// The same over two weights stacked by rows: columns n < N1 from B [N1, K], the rest from B2 [N2, K]
+// (N1, N2 multiples of 32); part[s][m][N1 + N2].
+hipError_t launch_splitk_gemm2(int M, int N1, int N2, int K, int nsplit, const uint16_t* A, const uint16_t* B,
+                               const uint16_t* B2, float* part, hipStream_t stream);
 
 // Query path with W_UQ W_UK absorbed ahead of time: the prepared weight w_q = head h's rows
 // [W_UQK[h] = W_UK[h]^T W_UQ_nope[h] (512 rows); W_QR[h] (64 rows)] in MFMA operand order
@@ -148,6 +152,15 @@ hipError_t launch_prefill_expanded(const CacheView& cache, int batch, int n_head
 // part (eps, weight gamma [512]), then the RoPE rotation of k_R and the append, as launch_rope_append.
 // workspace: kv_down_workspace_bytes(num_tokens, dim) bytes (fp32 split partials).
 size_t kv_down_workspace_bytes(int num_tokens, int dim);
+bool kv_down_tiled_path(int num_tokens);  // true where the tiled GEMM (not the split-K one) runs
+
+// launch_kv_down and launch_query_absorbed of the same tokens with shared launches (see query.hip).
+size_t kv_down_query_workspace_bytes(int num_tokens, int dim, int q_rank);
+hipError_t launch_kv_down_query(const CacheView& cache, int n_heads, int num_tokens, const int32_t* token_seq,
+                                const int32_t* token_pos, const uint16_t* x, int dim, const uint16_t* w_dkv,
+                                const uint16_t* gamma_kv, float eps_kv, const uint16_t* w_dq, const uint16_t* gamma_q,
+                                float eps_q, int q_rank, const uint16_t* w_q, float theta, void* workspace,
+                                uint16_t* q_abs, hipStream_t stream);
 hipError_t launch_kv_down(const CacheView& cache, int num_tokens, const int32_t* token_seq, const int32_t* token_pos,
                           const uint16_t* x, int dim, const uint16_t* w_dkv, const uint16_t* gamma, float eps,
                           float theta, void* workspace, hipStream_t stream);

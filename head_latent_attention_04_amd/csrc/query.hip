@@ -25,7 +25,7 @@
 //     mla_decode_absorbed takes.
 #include <algorithm>
 
-#include "rope_device.h"
+#include "finish_device.h"
 
 namespace mla {
 
@@ -34,7 +34,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kQrankMax = 2048;
-constexpr int kMaxQSplits = kGemmMaxSplits;
 
 // Prepared query weight: head h's 576 rows (W_UQK[h] rows 0..511, then the q_R rows of W_UQ) in MFMA
 // operand order: row n, element k at
@@ -43,11 +42,7 @@ constexpr int kMaxQSplits = kGemmMaxSplits;
 __host__ __device__ inline int64_t wq_offset(int h, int n, int k, int q_rank) {
   return ((((int64_t)h * (kRow / 32) + n / 32) * (q_rank / 16) + k / 16) * 64 + n % 32 + 32 * ((k / 8) & 1)) * 8 + k % 8;
 }
-// c_q in the same order for 32-token blocks: token t, element k at
-//   (((t / 32) * (q_rank / 16) + k / 16) * 64 + t % 32 + 32 ((k / 8) % 2)) * 8 + k % 8.
-__host__ __device__ inline int64_t cq_offset(int t, int k, int q_rank) {
-  return (((int64_t)(t / 32) * (q_rank / 16) + k / 16) * 64 + t % 32 + 32 * ((k / 8) & 1)) * 8 + k % 8;
-}
+// c_q is in the same order for 32-token blocks (cq_offset, finish_device.h).
 
 struct QueryWorkspace {
   size_t part, cq, cs, total;
@@ -118,7 +113,7 @@ __global__ void __launch_bounds__(256) absorb_query_weights_kernel(int q_rank, c
   }
 }
 
-// ---- c_q: split sums, RMSNorm; RoPE angles ------------------------------------------------------------
+// ---- c_q: split sums, RMSNorm; RoPE angles (cq_finish_token, finish_device.h) ---------------------------
 __global__ void __launch_bounds__(256) cq_finish_kernel(int num_tokens, int q_rank, int nsplit,
                                                         const int32_t* __restrict__ token_pos,
                                                         const float* __restrict__ part,
@@ -126,55 +121,8 @@ __global__ void __launch_bounds__(256) cq_finish_kernel(int num_tokens, int q_ra
                                                         double log2_theta, uint16_t* __restrict__ c_q,
                                                         double* __restrict__ cs) {
   __shared__ float s_sum[4];
-  const int i = blockIdx.x, tid = threadIdx.x;
-  const int n4 = q_rank / 4;  // float4 columns, <= 512
-  // thread t owns columns 4 (t + 256 u) .. +3, u < 2; all split loads are issued before the adds
-  float kv[2][4] = {};
-  float ss = 0.f;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c4 = tid + 256 * u;
-    if (c4 >= n4) continue;
-    const float4* p4 = reinterpret_cast<const float4*>(part) + (int64_t)i * n4 + c4;
-    float4 v[kMaxQSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxQSplits; ++s)
-      v[s] = s < nsplit ? p4[(int64_t)s * num_tokens * n4] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int s = 0; s < kMaxQSplits; ++s) {
-      kv[u][0] += v[s].x;
-      kv[u][1] += v[s].y;
-      kv[u][2] += v[s].z;
-      kv[u][3] += v[s].w;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kv[u][e] = bf16_to_f32(f32_to_bf16(kv[u][e]));  // wq_a's output dtype
-      ss += kv[u][e] * kv[u][e];
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((tid & 63) == 0) s_sum[tid >> 6] = ss;
-  // the token's RoPE angles (fp64), one pair per thread of the first 32
-  if (tid < kDr / 2) {
-    double c, s;
-    rope_cos_sin(token_pos[i], tid, log2_theta, &c, &s);
-    cs[((int64_t)i * (kDr / 2) + tid) * 2] = c;
-    cs[((int64_t)i * (kDr / 2) + tid) * 2 + 1] = s;
-  }
-  __syncthreads();
-  const float r = 1.f / sqrtf((s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3]) / q_rank + eps);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c4 = tid + 256 * u;
-    if (c4 >= n4) continue;
-    uint16_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(kv[u][e] * r * bf16_to_f32(gamma[4 * c4 + e]));
-    *reinterpret_cast<uint2*>(c_q + cq_offset(i, 4 * c4, q_rank)) =
-        make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-  }
+  cq_finish_token(blockIdx.x, num_tokens, q_rank, nsplit, token_pos, part, q_rank, gamma, eps, log2_theta, c_q, cs,
+                  s_sum);
 }
 
 // ---- q_abs rows -----------------------------------------------------------------------------------
@@ -239,6 +187,17 @@ __global__ void __launch_bounds__(256) query_gemm_kernel(int num_tokens, int n_h
 
 size_t query_workspace_bytes(int num_tokens, int dim, int q_rank) { return query_layout(num_tokens, dim, q_rank).total; }
 
+namespace {
+hipError_t launch_query_rows(int n_heads, int num_tokens, int q_rank, const uint16_t* c_q, const uint16_t* w_q,
+                             const double* cs, uint16_t* q_abs, hipStream_t stream) {
+  const int tblocks = (num_tokens + 31) / 32;
+  if (tblocks > 65535 || n_heads > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(query_gemm_kernel, dim3(kRow / 32, n_heads, tblocks), dim3(256), 0, stream, num_tokens, n_heads,
+                     q_rank, c_q, w_q, cs, q_abs);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_absorb_query_weights(int n_heads, int q_rank, const uint16_t* w_uq, const uint16_t* w_uk,
                                        uint16_t* w_q, hipStream_t stream) {
   if (q_rank % 64 != 0 || q_rank > kQrankMax) return hipErrorInvalidValue;
@@ -264,11 +223,85 @@ hipError_t launch_query_absorbed(int n_heads, int num_tokens, const int32_t* tok
   hipLaunchKernelGGL(cq_finish_kernel, dim3(num_tokens), dim3(256), 0, stream, num_tokens, q_rank, ns, token_pos, part,
                      gamma_q, eps, log2((double)theta), c_q, cs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int tblocks = (num_tokens + 31) / 32;
-  if (tblocks > 65535 || n_heads > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(query_gemm_kernel, dim3(kRow / 32, n_heads, tblocks), dim3(256), 0, stream, num_tokens, n_heads,
-                     q_rank, c_q, w_q, cs, q_abs);
-  return hipGetLastError();
+  return launch_query_rows(n_heads, num_tokens, q_rank, c_q, w_q, cs, q_abs, stream);
+}
+
+// ---- the KV down-projection and the absorbed query rows of the same tokens, launches shared -----------
+// Both down-projections read x: one split-K GEMM over the stacked weights [W_DKV; W_DQ] (fp32 partials
+// [split][token][576 + q_rank]), one finishing launch (work-groups 0 .. T-1 the KV side of token i,
+// T .. 2T-1 its query side), then the query GEMM: three launches instead of five. The split count is
+// the smaller of the two single-projection counts, so where those agree every result is bit for bit
+// that of launch_kv_down followed by launch_query_absorbed. Token counts that take the tiled KV GEMM
+// run the two paths one after the other.
+__global__ void __launch_bounds__(256) kv_q_finish_kernel(CacheView cache, int num_tokens, int q_rank, int nsplit,
+                                                          const int32_t* __restrict__ token_seq,
+                                                          const int32_t* __restrict__ token_pos,
+                                                          const float* __restrict__ part,
+                                                          const uint16_t* __restrict__ gamma_kv, float eps_kv,
+                                                          const uint16_t* __restrict__ gamma_q, float eps_q,
+                                                          double log2_theta, uint16_t* __restrict__ c_q,
+                                                          double* __restrict__ cs) {
+  __shared__ float s_sum[4];
+  const int ld = kKvRowOut + q_rank;
+  if ((int)blockIdx.x < num_tokens)
+    kv_finish_token(cache, blockIdx.x, num_tokens, nsplit, token_seq, token_pos, part, ld, gamma_kv, eps_kv,
+                    log2_theta, s_sum);
+  else
+    cq_finish_token(blockIdx.x - num_tokens, num_tokens, q_rank, nsplit, token_pos, part + kKvRowOut, ld, gamma_q,
+                    eps_q, log2_theta, c_q, cs, s_sum);
+}
+
+namespace {
+int kvq_splits(int num_tokens, int dim, int q_rank) {
+  return std::min(splitk_splits(num_tokens, kKvRowOut, dim), splitk_splits(num_tokens, q_rank, dim));
+}
+
+QueryWorkspace kvq_layout(int num_tokens, int dim, int q_rank) {
+  QueryWorkspace w;
+  const size_t ns = (size_t)kvq_splits(num_tokens, dim, q_rank);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  w.part = 0;
+  w.cq = al(ns * num_tokens * (kKvRowOut + q_rank) * 4);
+  w.cs = w.cq + al((size_t)((num_tokens + 31) / 32) * 32 * q_rank * 2);
+  w.total = w.cs + al((size_t)num_tokens * (kDr / 2) * 2 * sizeof(double));
+  return w;
+}
+
+size_t aligned256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+size_t kv_down_query_workspace_bytes(int num_tokens, int dim, int q_rank) {
+  if (kv_down_tiled_path(num_tokens))
+    return aligned256(kv_down_workspace_bytes(num_tokens, dim)) + query_workspace_bytes(num_tokens, dim, q_rank);
+  return kvq_layout(num_tokens, dim, q_rank).total;
+}
+
+hipError_t launch_kv_down_query(const CacheView& cache, int n_heads, int num_tokens, const int32_t* token_seq,
+                                const int32_t* token_pos, const uint16_t* x, int dim, const uint16_t* w_dkv,
+                                const uint16_t* gamma_kv, float eps_kv, const uint16_t* w_dq, const uint16_t* gamma_q,
+                                float eps_q, int q_rank, const uint16_t* w_q, float theta, void* workspace,
+                                uint16_t* q_abs, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  if (q_rank % 64 != 0 || q_rank > kQrankMax || dim % 64 != 0) return hipErrorInvalidValue;
+  char* ws = static_cast<char*>(workspace);
+  if (kv_down_tiled_path(num_tokens)) {
+    hipError_t e = launch_kv_down(cache, num_tokens, token_seq, token_pos, x, dim, w_dkv, gamma_kv, eps_kv, theta, ws,
+                                  stream);
+    if (e != hipSuccess) return e;
+    return launch_query_absorbed(n_heads, num_tokens, token_pos, x, dim, w_dq, gamma_q, eps_q, q_rank, w_q, theta,
+                                 ws + aligned256(kv_down_workspace_bytes(num_tokens, dim)), q_abs, stream);
+  }
+  const QueryWorkspace lay = kvq_layout(num_tokens, dim, q_rank);
+  float* part = reinterpret_cast<float*>(ws + lay.part);
+  uint16_t* c_q = reinterpret_cast<uint16_t*>(ws + lay.cq);
+  double* cs = reinterpret_cast<double*>(ws + lay.cs);
+  const int ns = kvq_splits(num_tokens, dim, q_rank);
+  hipError_t e = launch_splitk_gemm2(num_tokens, kKvRowOut, q_rank, dim, ns, x, w_dkv, w_dq, part, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kv_q_finish_kernel, dim3(2 * num_tokens), dim3(256), 0, stream, cache, num_tokens, q_rank, ns,
+                     token_seq, token_pos, part, gamma_kv, eps_kv, gamma_q, eps_q, log2((double)theta), c_q, cs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_query_rows(n_heads, num_tokens, q_rank, c_q, w_q, cs, q_abs, stream);
 }
 
 }  // namespace mla

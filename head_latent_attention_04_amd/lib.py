@@ -61,6 +61,10 @@ EXPORTS = {
     "mla_chunked_prefill_expanded": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp,
                                                     _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "mla_kv_down_append_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32]),
+    "mla_kv_down_query_absorbed_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32, _i32]),
+    "mla_kv_down_query_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp,
+                                                  _vp, _i32, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_float,
+                                                  _i32, _vp, _vp, _sz, _vp, _vp]),
     "mla_kv_down_append": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _vp, _i32,
                                           _vp, _vp, ctypes.c_float, _vp, _sz, _vp]),
     "mla_decode_plan": (ctypes.c_int, [ctypes.POINTER(MlaDims), _i32, _i32, _i32, ctypes.POINTER(_i32),
@@ -281,6 +285,28 @@ def kv_down_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, x, w_dk
         _ptr(w_dkv, "w_dkv", BF16, (dims.d_c + dims.d_rope) * dim), _ptr(gamma, "gamma", BF16, dims.d_c), eps,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_kv_down_append", st)
+
+
+def kv_down_query_absorbed_workspace_size(dims: MlaDims, num_tokens: int, dim: int, q_rank: int) -> int:
+    return int(load().mla_kv_down_query_absorbed_workspace_size(ctypes.byref(dims), num_tokens, dim, q_rank))
+
+
+def kv_down_query_absorbed(dims: MlaDims, cache: MlaCache, token_seq, token_pos, x, w_dkv, gamma_kv, eps_kv: float,
+                           w_dq, gamma_q, eps_q: float, w_q, workspace, q_abs, stream=None):
+    """mla_kv_down_append and mla_query_absorbed of the same tokens in one call (shared launches)."""
+    T = token_seq.numel()
+    H = dims.n_heads
+    dim = x.shape[1] if x.dim() == 2 else 0
+    r = w_dq.shape[0] if w_dq.dim() == 2 else 0
+    st = load().mla_kv_down_query_absorbed(
+        ctypes.byref(dims), _cache(cache), T, _ptr(token_seq, "token_seq", I32, T),
+        _ptr(token_pos, "token_pos", I32, T), _ptr(x, "x", BF16, T * dim), dim,
+        _ptr(w_dkv, "w_dkv", BF16, (dims.d_c + dims.d_rope) * dim), _ptr(gamma_kv, "gamma_kv", BF16, dims.d_c), eps_kv,
+        _ptr(w_dq, "w_dq", BF16, r * dim), _ptr(gamma_q, "gamma_q", BF16, r), eps_q, r,
+        _ptr(w_q, "w_q", BF16, H * (dims.d_c + dims.d_rope) * r),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(q_abs, "q_abs", BF16, T * H * (dims.d_c + dims.d_rope)), _stream(stream))
+    _check("mla_kv_down_query_absorbed", st)
 
 
 def decode_plan(dims: MlaDims, batch: int, max_seq_len: int, num_cus: int) -> Tuple[int, int]:

@@ -360,6 +360,34 @@ int mla_query_absorbed(const mla_dims* dims, int32_t num_tokens, const int32_t* 
                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mla_kv_down_query_absorbed - mla_kv_down_append and mla_query_absorbed of the same new tokens in one
+ * call, the two projections of the hidden state that come before the attention ("论文复现工坊 No.4",
+ * section 2: wkv_a with kv_norm on the latent part, wq_a with q_norm, then wq_b; section 4: the key
+ * up-projection absorbed into the query). Results: the cache rows exactly as mla_kv_down_append
+ * writes them and q_abs exactly as mla_query_absorbed writes it (bit for bit wherever the two calls
+ * split the input dimension the same way, as at 32 tokens of width 4096 with q_rank 512).
+ *   Arguments as the two calls: cache, token_seq, token_pos, x [num_tokens, dim], w_dkv, gamma_kv
+ *   and eps_kv as mla_kv_down_append's w_dkv, gamma and eps; w_dq, gamma_q, eps_q, q_rank, w_q and
+ *   q_abs as mla_query_absorbed's;
+ *   workspace >= mla_kv_down_query_absorbed_workspace_size(dims, num_tokens, dim, q_rank) bytes,
+ *   256-byte aligned; x, w_dkv, w_dq, w_q 16-byte aligned, q_abs 8-byte aligned;
+ *   num_tokens <= 2097120.
+ * Errors: MLA_ERR_NULL for a missing pointer, MLA_ERR_BAD_ARG for a negative count, a bad eps, a
+ * small or misaligned buffer, MLA_ERR_UNSUPPORTED for dim or q_rank not a multiple of 64 or
+ * q_rank > 2048. The size query returns 0 for arguments the call would reject.
+ * Below 256 tokens three launches on `stream` (one split-K GEMM over both weights, one finishing
+ * launch for both paths, the query GEMM) instead of the two calls' five; from 256 tokens the two
+ * calls' launches one after the other. num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+size_t mla_kv_down_query_absorbed_workspace_size(const mla_dims* dims, int32_t num_tokens, int32_t dim,
+                                                 int32_t q_rank);
+int mla_kv_down_query_absorbed(const mla_dims* dims, const mla_cache* cache, int32_t num_tokens,
+                               const int32_t* token_seq, const int32_t* token_pos, const uint16_t* x, int32_t dim,
+                               const uint16_t* w_dkv, const uint16_t* gamma_kv, float eps_kv, const uint16_t* w_dq,
+                               const uint16_t* gamma_q, float eps_q, int32_t q_rank, const uint16_t* w_q,
+                               void* workspace, size_t workspace_bytes, uint16_t* q_abs, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mla_chunked_prefill_expanded - the same causal chunked prefill as mla_chunked_prefill, computed in
  * the expanded form ("Multi-Head Latent Attention: DeepSeek V2/V3 工程视角" names the up-projection
  * of the latent cache and its absorbed equivalent as the two ways to attend; "论文复现工坊 No.4",

@@ -181,6 +181,51 @@ def test_query_path_validation_and_workspace():
     assert lib.query_absorbed_workspace_size(d, 32, 100, 512) == 0
 
 
+def kvq(dims, c, T=1, dim=4096, r=512, eps_kv=1e-6, eps_q=1e-6, ptrs=(FAKE,) * 8, ws=FAKE, wsb=1 << 40, out=FAKE):
+    """mla_kv_down_query_absorbed; ptrs = token_seq, token_pos, x, w_dkv, gamma_kv, w_dq, gamma_q, w_q."""
+    p = ptrs
+    return lib.load().mla_kv_down_query_absorbed(ctypes.byref(dims), ctypes.byref(c), T, p[0], p[1], p[2], dim, p[3],
+                                                 p[4], eps_kv, p[5], p[6], eps_q, r, p[7], ws, wsb, out, None)
+
+
+def test_kv_down_query_validation_and_workspace():
+    d = D()
+    assert kvq(d, cache(), dim=100) == lib.MLA_ERR_UNSUPPORTED
+    assert kvq(d, cache(), r=100) == lib.MLA_ERR_UNSUPPORTED
+    assert kvq(d, cache(), r=4096) == lib.MLA_ERR_UNSUPPORTED
+    assert kvq(d, cache(), dim=0) == lib.MLA_ERR_BAD_ARG
+    assert kvq(d, cache(), r=0) == lib.MLA_ERR_BAD_ARG
+    assert kvq(d, cache(), T=-1) == lib.MLA_ERR_BAD_ARG
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert kvq(d, cache(), eps_kv=eps) == lib.MLA_ERR_BAD_ARG
+        assert kvq(d, cache(), eps_q=eps) == lib.MLA_ERR_BAD_ARG
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert kvq(d, cache(), ptrs=tuple(ptrs)) == lib.MLA_ERR_NULL, i
+    assert kvq(d, cache(), ws=None) == lib.MLA_ERR_NULL
+    assert kvq(d, cache(), out=None) == lib.MLA_ERR_NULL
+    assert kvq(d, cache(data=None)) == lib.MLA_ERR_NULL
+    assert kvq(d, cache(), wsb=1000) == lib.MLA_ERR_BAD_ARG
+    assert kvq(d, cache(), ws=FAKE + 16) == lib.MLA_ERR_BAD_ARG
+    for i in (2, 3, 5, 7):  # x, w_dkv, w_dq, w_q: 16 bytes
+        ptrs = [FAKE] * 8
+        ptrs[i] = FAKE + 8
+        assert kvq(d, cache(), ptrs=tuple(ptrs)) == lib.MLA_ERR_BAD_ARG, i
+    assert kvq(d, cache(), out=FAKE + 4) == lib.MLA_ERR_BAD_ARG  # q_abs: 8 bytes
+    assert kvq(d, cache(), T=0, ptrs=(None,) * 8, ws=None, wsb=0, out=None) == lib.MLA_OK
+    assert kvq(D(n_heads=120), cache()) == lib.MLA_ERR_UNSUPPORTED
+    # 32 tokens, width 4096, rank 512: partials of 16 splits over the 576 + 512 stacked columns, c_q (one
+    # 32-token block), 32 cos/sin pairs per token
+    assert lib.kv_down_query_absorbed_workspace_size(d, 32, 4096, 512) == \
+        16 * 32 * 1088 * 4 + 32 * 512 * 2 + 32 * 32 * 16
+    # from 256 tokens the two calls' workspaces one after the other
+    assert lib.kv_down_query_absorbed_workspace_size(d, 2048, 4096, 512) == \
+        lib.kv_down_append_workspace_size(d, 2048, 4096) + lib.query_absorbed_workspace_size(d, 2048, 4096, 512)
+    assert lib.kv_down_query_absorbed_workspace_size(d, 32, 100, 512) == 0
+    assert lib.kv_down_query_absorbed_workspace_size(d, 32, 4096, 100) == 0
+
+
 MIS16 = FAKE + 8   # 8-byte aligned, not 16
 MIS8 = FAKE + 4    # 4-byte aligned, not 8
 MIS4 = FAKE + 2    # 2-byte aligned, not 4

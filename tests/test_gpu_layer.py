@@ -4,6 +4,7 @@ fp64 oracle's chain of the same steps.
 x [32, 4096] (the hidden state of the step's 32 new tokens, one per sequence at position 4095):
   mla_kv_down_append      c_KV = kv_norm(x W_DKV^T)[latent], k_R rotated, appended at 4095
   mla_query_absorbed      q_abs rows from x through W_DQ, q_norm and the pre-multiplied W_UQ W_UK
+                          (or both in one mla_kv_down_query_absorbed call)
   mla_decode_absorbed     split-KV attention over the 4096 cached tokens (planner's split, 256 CUs)
   mla_decode_combine      log-sum-exp merge and W_UV
   mla_output_projection   wo on the flattened heads (weight prepared by mla_prepare_output_weight)
@@ -37,8 +38,10 @@ def _dev(a):
     return torch.from_numpy(a).to("cuda")
 
 
-def test_decode_layer_from_hidden_state():
-    say("[layer] x -> kv_down_append + query_absorbed -> decode_absorbed -> combine -> wo")
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_layer_from_hidden_state(fused):
+    """fused: the two projections of x through mla_kv_down_query_absorbed (one call, shared launches)."""
+    say(f"[layer] x -> kv_down_append + query_absorbed (fused={fused}) -> decode_absorbed -> combine -> wo")
     case = make_config(1)
     B, H = case.batch, case.n_heads
     kin = make_kv_down_inputs(501, B, DIM)
@@ -59,12 +62,19 @@ def test_decode_layer_from_hidden_state():
     w_o_prep = torch.empty_like(d["w_o"])
     lib.prepare_output_weight(dims, d["w_o"], w_o_prep)
     # the layer step
-    ws_kv = torch.empty(max(256, lib.kv_down_append_workspace_size(dims, B, DIM)), dtype=torch.uint8, device="cuda")
-    lib.kv_down_append(dims, dc.cache, d["seq"], d["pos"], d["x"], d["w_dkv"], d["gamma"], EPS, ws_kv)
-    ws_q = torch.empty(max(256, lib.query_absorbed_workspace_size(dims, B, DIM, Q_RANK)), dtype=torch.uint8,
-                       device="cuda")
     q_abs = torch.empty((B, H, 576), dtype=torch.int16, device="cuda")
-    lib.query_absorbed(dims, d["pos"], d["x"], d["w_dq"], d["gq"], EPS, w_q, ws_q, q_abs)
+    if fused:
+        ws = torch.empty(lib.kv_down_query_absorbed_workspace_size(dims, B, DIM, Q_RANK), dtype=torch.uint8,
+                         device="cuda")
+        lib.kv_down_query_absorbed(dims, dc.cache, d["seq"], d["pos"], d["x"], d["w_dkv"], d["gamma"], EPS, d["w_dq"],
+                                   d["gq"], EPS, w_q, ws, q_abs)
+    else:
+        ws_kv = torch.empty(max(256, lib.kv_down_append_workspace_size(dims, B, DIM)), dtype=torch.uint8,
+                            device="cuda")
+        lib.kv_down_append(dims, dc.cache, d["seq"], d["pos"], d["x"], d["w_dkv"], d["gamma"], EPS, ws_kv)
+        ws_q = torch.empty(max(256, lib.query_absorbed_workspace_size(dims, B, DIM, Q_RANK)), dtype=torch.uint8,
+                           device="cuda")
+        lib.query_absorbed(dims, d["pos"], d["x"], d["w_dq"], d["gq"], EPS, w_q, ws_q, q_abs)
     st, ns = dc.plan()
     dc.alloc_decode(ns)
     o_part, lse_part = dc.partials

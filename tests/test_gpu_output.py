@@ -89,8 +89,10 @@ def test_prepare_output_weight_is_the_operand_order(H, dim):
     assert np.array_equal(prep.cpu().numpy().view(np.uint16), operand_order(inp.w_o))
 
 
-@pytest.mark.parametrize("H,T,dim", [(16, 45, 320), (128, 32, 4096)])
+@pytest.mark.parametrize("H,T,dim", [(16, 45, 320), (16, 70, 192), (128, 32, 4096)])
 def test_output_projection_matches_oracle(H, T, dim):
+    """(16, 70, 192): three row blocks (the last of 6 rows) and six column tiles (the second
+    work-group has two active waves)."""
     say(f"[output] wo on the heads H={H} T={T} dim={dim}")
     inp = make_output_inputs(33, T, dim, H)
     dims = lib.make_dims(H)
@@ -135,10 +137,12 @@ def test_fold_output_weights_matches_oracle(H, dim):
 
 
 @pytest.mark.parametrize("H,T,dim,device_weights", [(16, 45, 320, False), (16, 45, 320, True),
-                                                    (128, 32, 4096, True)])
+                                                    (16, 70, 192, True), (128, 32, 4096, True)])
 def test_output_folded_matches_oracle(H, T, dim, device_weights):
     """The folded projection; at full size the weight is the device-prepared one and the outputs of 64
-    sampled columns are compared (the oracle folds those rows of wo only)."""
+    sampled columns are compared (the oracle folds those rows of wo only). (16, 70, 192): three row
+    blocks and a work-group with two active waves; at full size each split spans four chunks of the
+    activations."""
     say(f"[output] folded projection H={H} T={T} dim={dim} device weights={device_weights}")
     inp = make_output_inputs(35, T, dim, H)
     dims = lib.make_dims(H)
