@@ -39,8 +39,8 @@ COPY_PROBE_BYTES = 256 << 20
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -350,7 +350,7 @@ def main():
         "total_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_roofline_frac_hbm": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels_ms": {k: round(v, 5) for k, v in ms.items()},
-        "roofline": {"kernel": "decode_mfma_kernel<4, true> (split-KV attention, mla_decode_attend)", "bound": "hbm",
+        "roofline": {"kernel": "decode_mfma_kernel<4, true, true> (split-KV attention, mla_decode_attend)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": cache_bytes,
@@ -463,7 +463,7 @@ def decode_configs_main(args, torch, lib, props):
             "step_TFLOPs": round(flops / (ms_step * 1e-3) / 1e12, 1),
             "latent_kv_GBps_step": round(cache_bytes / (ms_step * 1e-3) / 1e9, 1),
             "kernels_ms": {"decode_attention": round(ms_attn, 5), "combine_wuv": round(ms_comb, 5)},
-            "roofline": {"kernel": "decode_mfma_kernel<4, true>", "bound": "hbm",
+            "roofline": {"kernel": "decode_mfma_kernel<4, true, true>", "bound": "hbm",
                          "achieved": round(cache_bytes / (ms_attn * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(cache_bytes / (ms_attn * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                          "algorithmic_bytes_per_launch": cache_bytes},
@@ -534,7 +534,7 @@ def prefill_main(args, torch, lib, props):
                                f"latent cache", "total_q": total_q, "n_heads": H, "d_c": 512, "d_rope": 64,
                    "d_nope": 128, "d_v": 128},
         "kernels_ms": {k: round(v, 4) for k, v in ms.items()},
-        "roofline": {"kernel": "mla_chunked_prefill (absorb + decode_mfma_kernel<4, false> causal rows + combine)",
+        "roofline": {"kernel": "mla_chunked_prefill (absorb + decode_mfma_kernel<4, false, false> causal rows + combine)",
                      "bound": "mfma", "achieved": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round((attn + proj) / (ms["chunked_prefill"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -141,23 +141,33 @@ __device__ __forceinline__ StageCopy stage_copy(const uint16_t* src_blk, int hal
   return c;
 }
 
-// One wave instruction of a stage copy: the tile of `band`.
+// One wave instruction of a stage copy: the tile of `band`. kNt: the rows are read by this work-group
+// only (decode with one head group), so the load carries the non-temporal hint and the stream does not
+// displace reused lines (queries, block table) from the caches; the prefill's rows are read by many
+// work-groups and keep the default policy.
+template <bool kNt>
 __device__ __forceinline__ void stage_copy_band(const StageCopy& c, int band) {
   const uint32_t soff = c.sbase + band * 128;
   const uint32_t m0 = c.m0base + band * 1024;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(c.voff), "s"(c.rsrc), "s"(m0),
-               "s"(soff)
-               : "memory", "m0");
+  if constexpr (kNt)
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds" ::"v"(c.voff), "s"(c.rsrc),
+                 "s"(m0), "s"(soff)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(c.voff), "s"(c.rsrc), "s"(m0),
+                 "s"(soff)
+                 : "memory", "m0");
 #pragma clang diagnostic pop
 }
 
+template <bool kNt>
 __device__ __forceinline__ void issue_stage(const uint16_t* src_blk, int half, uint32_t lds_stage, int valid, int wave,
                                             int lane) {
   const StageCopy c = stage_copy(src_blk, half, lds_stage, valid, wave, lane);
 #pragma unroll
-  for (int band = 0; band < kBands; ++band) stage_copy_band(c, band);
+  for (int band = 0; band < kBands; ++band) stage_copy_band<kNt>(c, band);
 }
 
 // for (I = B; I < E; ++I) f(I) with I a compile-time constant in every call: the register arrays the
@@ -265,9 +275,10 @@ template <int HT>
 constexpr int kPBytesOf = HT * 32 * kPHeadBytes;  // weights P of one stage
 
 // The work of one attention work-group (blockIdx.x: its logical block). HT: head tiles of 32 per
-// work-group (1..4); kOperandOrder: layout of q_abs (see mla_internal.h). smem_raw: the stage
-// buffers (kStages * kStageBytes, 1 KB aligned); p_raw: P of two stages (2 * kPBytesOf<HT>).
-template <int HT, bool kOperandOrder>
+// work-group (1..4); kOperandOrder: layout of q_abs (see mla_internal.h); kNt: the cache rows are
+// read once (stage_copy_band). smem_raw: the stage buffers (kStages * kStageBytes, 1 KB aligned);
+// p_raw: P of two stages (2 * kPBytesOf<HT>).
+template <int HT, bool kOperandOrder, bool kNt>
 __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads, int n_groups,
                                             const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q_lens,
                                             int batch, const uint16_t* __restrict__ q_abs, float scale_log2,
@@ -350,9 +361,11 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
   // register, so the compiler waits for every load here (the query, and stage 0 with it, which the
   // first step needs anyway) and knows the query is resident inside the loop; otherwise it would
   // guard each score MFMA with a wait that also drains the copies in flight. Stage 1 follows.
-  issue_stage(block_ptr(cache, b, blk0), 0, lds0, min(kStageTok, t1 - t0), wave, lane);
+  issue_stage<kNt>(block_ptr(cache, b, blk0), 0, lds0, min(kStageTok, t1 - t0), wave, lane);
   asm volatile("" ::"v"(qreg[35]));
-  if (nstages > 1) issue_stage(block_ptr(cache, b, blk0), 1, lds0 + kStageBytes, min(kStageTok, t1 - t0 - kStageTok), wave, lane);
+  if (nstages > 1)
+    issue_stage<kNt>(block_ptr(cache, b, blk0), 1, lds0 + kStageBytes, min(kStageTok, t1 - t0 - kStageTok), wave,
+                     lane);
 
   // Score operand: lane reads token row n at chunk 2 ks + kh, i.e. band ks/4 and slot
   // (2 (ks%4) + kh) ^ swz(n) = 2 (ks%4) ^ (kh ^ swz(n)): one per-lane base per ks % 4.
@@ -478,7 +491,7 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
         if constexpr (kReduce)
           static_for<ks * kScorePv / 36, (ks + 1) * kScorePv / 36>([&](auto I) { pv_mfma(stp, pp, decltype(I)::value); });
         if constexpr ((ks & 3) == 1) {
-          if (copy_next) stage_copy_band(cp, ks >> 2);
+          if (copy_next) stage_copy_band<kNt>(cp, ks >> 2);
         }
         // keep this order: the scheduler would otherwise hoist operand loads and run out of registers
         __builtin_amdgcn_sched_barrier(0);
@@ -609,7 +622,7 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
   }
 }
 
-template <int HT, bool kOperandOrder>
+template <int HT, bool kOperandOrder, bool kNt>
 __global__ void __launch_bounds__(kWaves * 64, 1)
 decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __restrict__ seq_lens,
                    const int32_t* __restrict__ cu_q_lens, int batch, const uint16_t* __restrict__ q_abs,
@@ -617,8 +630,8 @@ decode_mfma_kernel(CacheView cache, int n_heads, int n_groups, const int32_t* __
                    float* __restrict__ lse_partial) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * kStageBytes];
   __shared__ __attribute__((aligned(16))) char p_raw[2 * kPBytesOf<HT>];
-  attend_tile<HT, kOperandOrder>(cache, n_heads, n_groups, seq_lens, cu_q_lens, batch, q_abs, scale_log2, split_tokens,
-                                 num_splits, o_partial, lse_partial, smem_raw, p_raw);
+  attend_tile<HT, kOperandOrder, kNt>(cache, n_heads, n_groups, seq_lens, cu_q_lens, batch, q_abs, scale_log2,
+                                      split_tokens, num_splits, o_partial, lse_partial, smem_raw, p_raw);
 }
 
 
@@ -629,9 +642,15 @@ static hipError_t launch_ht(const CacheView& cache, int rows, int n_heads, const
   const int groups = (q_tiles(n_heads) + 3) / 4;
   const int64_t nwg = (int64_t)groups * num_splits * rows;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_mfma_kernel<HT, kOperandOrder>), dim3((unsigned)nwg), dim3(kWaves * 64), 0, stream, cache,
-                     n_heads, groups, seq_lens, cu_q_lens, batch, q_abs, scale * kLog2e, split_tokens, num_splits,
-                     o_partial, lse_partial);
+  // decode with one head group reads every cache row once; prefill rows and several head groups re-read
+  if (cu_q_lens == nullptr && groups == 1)
+    hipLaunchKernelGGL((decode_mfma_kernel<HT, kOperandOrder, true>), dim3((unsigned)nwg), dim3(kWaves * 64), 0, stream,
+                       cache, n_heads, groups, seq_lens, cu_q_lens, batch, q_abs, scale * kLog2e, split_tokens,
+                       num_splits, o_partial, lse_partial);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<HT, kOperandOrder, false>), dim3((unsigned)nwg), dim3(kWaves * 64), 0,
+                       stream, cache, n_heads, groups, seq_lens, cu_q_lens, batch, q_abs, scale * kLog2e, split_tokens,
+                       num_splits, o_partial, lse_partial);
   return hipGetLastError();
 }
 
