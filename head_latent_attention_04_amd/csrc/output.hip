@@ -167,31 +167,45 @@ __global__ void __launch_bounds__(256) oo_splitk_gemm_kernel(int M, int N, int64
   for (int64_t k0 = kbeg; k0 < kend; k0 += kOoChunk) {
     const int klen = (int)std::min<int64_t>(kOoChunk, kend - k0);  // a multiple of 16
     if (k0 != kbeg) __syncthreads();                              // the previous chunk is consumed
-    for (int i = tid; i < 32 * (klen / 8); i += 256) {
-      const int r = i / (klen / 8), c = i % (klen / 8);
+    auto stage_act = [&](int i, int cpr) {  // 16 bytes: row i / cpr, chunk i % cpr
+      const int r = i / cpr, c = i % cpr;
       const int row = std::min(32 * tb + r, M - 1);
       *reinterpret_cast<uint4*>(sa + r * kOoPitch + 16 * c) =
           *reinterpret_cast<const uint4*>(act + (int64_t)row * K + k0 + 8 * c);
+    };
+    if (klen == kOoChunk) {
+#pragma unroll 4
+      for (int i = tid; i < 32 * (kOoChunk / 8); i += 256) stage_act(i, kOoChunk / 8);
+    } else {
+      for (int i = tid; i < 32 * (klen / 8); i += 256) stage_act(i, klen / 8);
     }
     __syncthreads();
     if (active) {
       const uint16_t* pk = pb + (k0 / 16) * 512;
-      const int steps = klen / 16;
-      int k = 0;
-      for (; k + 8 <= steps; k += 8) {
+      // eight weight fragments in flight; each is read by this wave only, hence the non-temporal hint
+      auto batch = [&](int k) {
         bf16x8 b[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) b[u] = *reinterpret_cast<const bf16x8*>(pk + (int64_t)(k + u) * 512);
+        for (int u = 0; u < 8; ++u)
+          b[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(pk + (int64_t)(k + u) * 512));
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * (k + u));
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[u], acc, 0, 0, 0);
         }
-      }
-      for (; k < steps; ++k) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(pk + (int64_t)k * 512);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      };
+      if (klen == kOoChunk) {  // a whole chunk: the step count is a constant and the loop unrolls
+#pragma unroll
+        for (int k = 0; k < kOoChunk / 16; k += 8) batch(k);
+      } else {
+        const int steps = klen / 16;
+        int k = 0;
+        for (; k + 8 <= steps; k += 8) batch(k);
+        for (; k < steps; ++k) {
+          const bf16x8 b = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(pk + (int64_t)k * 512));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
       }
     }
   }

@@ -146,7 +146,8 @@ __global__ void __launch_bounds__(256) query_gemm_kernel(int num_tokens, int n_h
     for (int u = 0; u < 8; ++u) {
       if (k + u < steps) {
         a[u] = *reinterpret_cast<const bf16x8*>(pa + (k + u) * 512);
-        b[u] = *reinterpret_cast<const bf16x8*>(pb + (k + u) * 512);
+        // the prepared weight is read once per call: non-temporal hint
+        b[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(pb + (k + u) * 512));
       }
     }
 #pragma unroll
