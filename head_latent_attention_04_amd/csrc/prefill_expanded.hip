@@ -94,6 +94,28 @@ __device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
 // chunk) land on distinct bank groups.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ uint32_t seg_off(int row, int chunk) { return row * kSeg + 16 * (chunk ^ swz(row)); }
+// Swizzle of the value sub-tiles, which only transposing reads touch: one read instruction covers rows
+// r0 .. r0 + 7 (two groups of four) at four adjacent chunks, and rows r and r + 2 must then differ in
+// bit 2 of the swizzle to reach different banks; the rotation of the row within its 8 does that (swz
+// above left rows r, r + 2 2-way conflicted: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE 0.50 -> 0 on a
+// kernel that issues exactly these reads).
+__device__ __forceinline__ int swz_v(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Lanes l and l ^ 32 hold the low and high 8 bytes of four 16-byte chunks: x[2q], x[2q + 1] the lane's
+// half of chunk q. After the exchange the low lane holds whole chunks 0 (c[0]) and 1 (c[1]), the high
+// lane whole chunks 2 and 3 (v_permlane32_swap hands the low lane the high lane's first operand and the
+// high lane the low lane's second operand), so each stores 16-byte pieces.
+__device__ __forceinline__ void pair_chunks(const uint32_t (&x)[8], u32x4 (&c)[2]) {
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x[k], x[k + 4], false, false);
+    lo[k] = r[0];
+    hi[k] = r[1];
+  }
+  c[0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  c[1] = u32x4{lo[2], lo[3], hi[2], hi[3]};
+}
 
 // Work-groups go to the XCDs round-robin by id; logical index L runs contiguously on one XCD.
 __device__ __forceinline__ int xcd_logical(int h, int G) {
@@ -223,18 +245,28 @@ __global__ void __launch_bounds__(512) upproj_kernel(CacheView cache, const int3
   // K_up and of V_up). D layout: lane holds token column lane % 32 and weight rows
   // 8 (e / 4) + 4 (lane / 32) + e % 4 of a block, i.e. four consecutive outputs per (block, e / 4).
   wg_barrier();  // every wave is done reading the stages
+  // The lane pair (l, l ^ 32) (the same token, columns 4 khalf .. +3 of each 8) trades halves so that
+  // every staging store is a whole 16-byte piece: the 8-byte stores of the halves were 2-way bank
+  // conflicted at this pitch (tokens t and t + 16 of 32 lanes on the same banks).
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int tl = 64 * wm + 32 * i + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      uint32_t x[8];
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int col = 128 * wn + 32 * j + 8 * e4 + 4 * khalf;
-        const u32x2 v = {pack_bf16x4_lo(acc[j][i][4 * e4], acc[j][i][4 * e4 + 1]),
-                         pack_bf16x4_lo(acc[j][i][4 * e4 + 2], acc[j][i][4 * e4 + 3])};
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + tl * kUpOutPitch + 2 * col) = v;
+        x[2 * e4] = pack_bf16x4_lo(acc[j][i][4 * e4], acc[j][i][4 * e4 + 1]);
+        x[2 * e4 + 1] = pack_bf16x4_lo(acc[j][i][4 * e4 + 2], acc[j][i][4 * e4 + 3]);
       }
+      u32x4 chunk[2];
+      pair_chunks(x, chunk);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = 128 * wn + 32 * j + 8 * (2 * khalf + t);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + tl * kUpOutPitch + 2 * col) = chunk[t];
+      }
+    }
   }
   wg_barrier();
   const int64_t kvbase = ((int64_t)(b * n_heads + h) * lpad + m0) * kDnope;
@@ -320,11 +352,12 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
     const int r = 8 * wave + (lv >> 3);
     const int c16 = 16 * ((lv & 7) ^ swz(r));
     const uint32_t okv = (uint32_t)(r * kDnope * 2 + c16);
+    const uint32_t ov = (uint32_t)(r * kDnope * 2 + 16 * ((lv & 7) ^ swz_v(r)));  // value sub-tiles
     copy_seg(rk, okv, 0, __builtin_amdgcn_readfirstlane(buf + 0 * kFaSub));
     copy_seg(rk, okv + kSeg, 0, __builtin_amdgcn_readfirstlane(buf + 1 * kFaSub));
     copy_seg(rr, (uint32_t)(r * kRowBytes + kDc * 2 + c16), 0, __builtin_amdgcn_readfirstlane(buf + 2 * kFaSub));
-    copy_seg(rv, okv, 0, __builtin_amdgcn_readfirstlane(buf + 3 * kFaSub));
-    copy_seg(rv, okv + kSeg, 0, __builtin_amdgcn_readfirstlane(buf + 4 * kFaSub));
+    copy_seg(rv, ov, 0, __builtin_amdgcn_readfirstlane(buf + 3 * kFaSub));
+    copy_seg(rv, ov + kSeg, 0, __builtin_amdgcn_readfirstlane(buf + 4 * kFaSub));
   };
 
   // K operand (A): key row 32 kb + lane % 32, elements 16 ks + 8 khalf: sub-tile ks / 4 (ks < 8) or
@@ -405,7 +438,7 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
 #pragma unroll
           for (int rd = 0; rd < 2; ++rd) {
             const int r = 32 * kb + 16 * half + 8 * rd + 4 * (g16 >> 1) + (r16 >> 2);
-            t[rd] = lds_tr16(buf + sub * kFaSub + r * kSeg + 16 * (chunk ^ swz(r)) + 8 * (r16 & 1));
+            t[rd] = lds_tr16(buf + sub * kFaSub + r * kSeg + 16 * (chunk ^ swz_v(r)) + 8 * (r16 & 1));
           }
           const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
           o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[half], o[j], 0, 0, 0);
