@@ -100,6 +100,10 @@ __device__ __forceinline__ uint32_t seg_off(int row, int chunk) { return row * k
 // above left rows r, r + 2 2-way conflicted: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE 0.50 -> 0 on a
 // kernel that issues exactly these reads).
 __device__ __forceinline__ int swz_v(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Swizzle of the attention's key sub-tiles: the same rotation, flipped by bit 3 of the row. The 16 rows
+// one LDS cycle serves at one chunk still fall on distinct bank groups, and rows 32 apart share a
+// swizzle, so every key-operand address is a per-lane base plus a compile-time offset.
+__device__ __forceinline__ int swz_k(int row) { return swz_v(row) ^ (2 * ((row >> 3) & 1)); }
 
 // Lanes l and l ^ 32 hold the low and high 8 bytes of four 16-byte chunks: x[2q], x[2q + 1] the lane's
 // half of chunk q. After the exchange the low lane holds whole chunks 0 (c[0]) and 1 (c[1]), the high
@@ -345,12 +349,12 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
     const i32x4 rv = buffer_rsrc(v_up + kv_base + (int64_t)t0 * kDnope, kFaKeys * kDnope * 2);
     const i32x4 rr = buffer_rsrc(block_base(cache, b, kt), kBlock * kRowBytes);
     // lane l lands at row r = 8 w + l / 8, slot l % 8 of each sub-tile, so it fetches chunk
-    // (l % 8) ^ swz(r); the offsets are recomputed here rather than held across the loop (the empty
-    // asm makes the lane index opaque at this point)
+    // (l % 8) ^ swz_k(r) (keys, k_R) or (l % 8) ^ swz_v(r) (values); the offsets are recomputed here
+    // rather than held across the loop (the empty asm makes the lane index opaque at this point)
     int lv = lane;
     asm volatile("" : "+v"(lv));
     const int r = 8 * wave + (lv >> 3);
-    const int c16 = 16 * ((lv & 7) ^ swz(r));
+    const int c16 = 16 * ((lv & 7) ^ swz_k(r));
     const uint32_t okv = (uint32_t)(r * kDnope * 2 + c16);
     const uint32_t ov = (uint32_t)(r * kDnope * 2 + 16 * ((lv & 7) ^ swz_v(r)));  // value sub-tiles
     copy_seg(rk, okv, 0, __builtin_amdgcn_readfirstlane(buf + 0 * kFaSub));
@@ -366,6 +370,22 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
   //   32 kb + 16 half + 8 rd + 4 (g / 2) + r / 4 at value column 32 j + 16 (g % 2) + 4 (r % 4)
   // and receives column 32 j + lane % 32 of 4 keys: the key order of the weights' B operand.
   const int g16 = lane >> 4, r16 = lane & 15;
+  // per-lane parts of the operand addresses; the rest of each address is a compile-time offset.
+  // Keys: row 32 kb + n (n = lane % 32) at chunk 2 m + khalf (m = ks % 4): n * 128 + 16 ((2 m +
+  // khalf) ^ swz_k(n)), plus 4096 kb. Values: row 8 q + rl (q = 4 kb + 2 half + rd, rl = 4 (g16 / 2) +
+  // r16 / 4 < 8) at chunk 4 (j % 2) + 2 (g16 % 2) + (r16 / 2) % 2, byte 8 (r16 % 2).
+  uint32_t kl[4], vl[2];
+  {
+    const int n = lane & 31, rl = 4 * (g16 >> 1) + (r16 >> 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kl[m] = (uint32_t)(n * kSeg + 16 * ((2 * m + khalf) ^ swz_k(n)));
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2)
+      vl[p2] = (uint32_t)(rl * kSeg + 16 * ((4 * p2 + 2 * (g16 & 1) + ((r16 >> 1) & 1)) ^ swz_v(rl)) + 8 * (r16 & 1));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(kl[m]));  // held, not recomputed in the loop
+    asm volatile("" : "+v"(vl[0]), "+v"(vl[1]));
+  }
   float m_ref = -INFINITY, lsum = 0.f;
   f32x16 o[4];
 #pragma unroll
@@ -391,7 +411,7 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) {
         const int sub = ks < 8 ? ks >> 2 : 2;
-        const bf16x8 kop = lds_b128(buf + sub * kFaSub + seg_off(32 * kb + (lane & 31), 2 * (ks & 3) + khalf));
+        const bf16x8 kop = lds_b128(buf + kl[ks & 3] + (sub * kFaSub + 32 * kb * kSeg));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sc, 0, 0, 0);
       }
       // softmax: lane holds query jq and keys t0 + 32 kb + 8 (e / 4) + 4 khalf + e % 4; the max is
@@ -431,15 +451,12 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int sub = 3 + (j >> 1);
-        const int chunk = 4 * (j & 1) + 2 * (g16 & 1) + ((r16 >> 1) & 1);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           i16x4 t[2];
 #pragma unroll
-          for (int rd = 0; rd < 2; ++rd) {
-            const int r = 32 * kb + 16 * half + 8 * rd + 4 * (g16 >> 1) + (r16 >> 2);
-            t[rd] = lds_tr16(buf + sub * kFaSub + r * kSeg + 16 * (chunk ^ swz_v(r)) + 8 * (r16 & 1));
-          }
+          for (int rd = 0; rd < 2; ++rd)
+            t[rd] = lds_tr16(buf + vl[j & 1] + (sub * kFaSub + (32 * kb + 16 * half + 8 * rd) * kSeg));
           const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
           o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[half], o[j], 0, 0, 0);
         }
