@@ -118,3 +118,66 @@ def test_decode_layer_from_hidden_state(fused):
     say(f"  lse: max |lse - lse oracle| = {ex:.2e}")
     assert ex <= 1e-3   # the reference already scores with the bf16 query rows the path defines
     assert_close(O.bf16_to_f64(y.cpu().numpy().view(np.uint16)), O.bf16_to_f64(y_ref), "y = wo(attention)")
+
+
+def test_decode_layer_graph_replay_matches_eager():
+    """The layer step (mla_kv_down_query_absorbed, mla_decode_absorbed, mla_decode_combine,
+    mla_output_projection: 7 launches) captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, reproduces the eager step bit for bit (y, lse, the appended
+    cache rows)."""
+    say("[layer] step in a HIP graph")
+    case = make_config(1)
+    B, H = case.batch, case.n_heads
+    kin = make_kv_down_inputs(511, B, DIM)
+    qin = make_query_inputs(512, B, DIM, H, Q_RANK)
+    oin = make_output_inputs(513, B, DIM, H)
+    pos = (case.seq_lens - 1).astype(np.int32)
+    seq = np.arange(B, dtype=np.int32)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dims = dc.dims
+    d = dict(x=_dev(kin.x), w_dkv=_dev(kin.w_dkv), gamma=_dev(kin.gamma), w_dq=_dev(qin.w_dq), gq=_dev(qin.gamma_q),
+             w_o=_dev(oin.w_o), pos=_dev(pos), seq=_dev(seq))
+    w_q = torch.empty(H * 576 * Q_RANK, dtype=torch.int16, device="cuda")
+    lib.absorb_query_weights(dims, _dev(qin.w_uq), _dev(qin.w_uk), w_q)
+    w_o_prep = torch.empty_like(d["w_o"])
+    lib.prepare_output_weight(dims, d["w_o"], w_o_prep)
+    ws = torch.empty(lib.kv_down_query_absorbed_workspace_size(dims, B, DIM, Q_RANK), dtype=torch.uint8, device="cuda")
+    ws_o = torch.empty(lib.output_projection_workspace_size(dims, B, DIM, False), dtype=torch.uint8, device="cuda")
+    q_abs = torch.empty((B, H, 576), dtype=torch.int16, device="cuda")
+    y = torch.empty((B, DIM), dtype=torch.int16, device="cuda")
+    st, ns = dc.plan()
+    dc.alloc_decode(ns)
+    o_part, lse_part = dc.partials
+
+    def step():
+        lib.kv_down_query_absorbed(dims, dc.cache, d["seq"], d["pos"], d["x"], d["w_dkv"], d["gamma"], EPS, d["w_dq"],
+                                   d["gq"], EPS, w_q, ws, q_abs)
+        lib.decode_absorbed(dims, dc.cache, dc.seq_lens, q_abs, st, ns, o_part, lse_part)
+        lib.decode_combine(dims, B, ns, o_part, lse_part, dc.w_uv, dc.out, dc.lse)
+        lib.output_projection(dims, dc.out, w_o_prep, DIM, False, ws_o, y)
+
+    step()
+    torch.cuda.synchronize()
+    ref_y, ref_lse, ref_cache = y.clone(), dc.lse.clone(), dc.cache_data.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(np.arange(B) * case.max_blocks_per_seq + 63).to("cuda")
+    for rep in range(4):
+        y.fill_(0)
+        dc.lse.fill_(0)
+        q_abs.fill_(0)
+        o_part.fill_(0)
+        dc.cache_data[rows, 63] = 0   # the appended rows, rewritten by each replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref_y), f"replay {rep}: y differs"
+        assert torch.equal(dc.lse, ref_lse), f"replay {rep}: lse differs"
+        assert torch.equal(dc.cache_data, ref_cache), f"replay {rep}: cache differs"
