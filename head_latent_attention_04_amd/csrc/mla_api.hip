@@ -300,6 +300,19 @@ int mla_kv_down_query_absorbed(const mla_dims* dims, const mla_cache* cache, int
                                             dims->rope_theta, workspace, q_abs, stream));
 }
 
+int mla_check_inputs(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                     const int32_t* cu_q_lens, int32_t total_q, int32_t* error_word, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0 || (cu_q_lens != nullptr && total_q < 0)) return MLA_ERR_BAD_ARG;
+  if (!error_word || (batch > 0 && !seq_lens)) return MLA_ERR_NULL;
+  if (!aligned(error_word, 4)) return MLA_ERR_BAD_ARG;
+  return launched(mla::launch_check_inputs(batch, seq_lens, cache->block_table, cache->max_blocks_per_seq,
+                                           cache->num_blocks, dims->block_size, cu_q_lens, total_q, error_word,
+                                           stream));
+}
+
 int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, int32_t num_cus,
                     int32_t* split_tokens, int32_t* num_splits) {
   int st = check_dims(dims);

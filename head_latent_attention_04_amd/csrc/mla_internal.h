@@ -165,6 +165,14 @@ hipError_t launch_kv_down(const CacheView& cache, int num_tokens, const int32_t*
                           const uint16_t* x, int dim, const uint16_t* w_dkv, const uint16_t* gamma, float eps,
                           float theta, void* workspace, hipStream_t stream);
 
+// Check of the caller's device-resident index data (one work-group): *error_word = OR of the kCheck*
+// bits of the rules broken, 0 when none. table == nullptr: the contiguous layout; cu_q_lens == nullptr:
+// decode (no chunk offsets).
+constexpr int kCheckBadLength = 1, kCheckBadBlock = 2, kCheckBadOffsets = 4, kCheckChunkTooLong = 8;
+hipError_t launch_check_inputs(int batch, const int32_t* seq_lens, const int32_t* table, int max_blocks,
+                               int64_t num_blocks, int block_size, const int32_t* cu_q_lens, int total_q,
+                               int32_t* error_word, hipStream_t stream);
+
 // LSE merge over splits + W_UV up-projection.
 hipError_t launch_combine(int batch, int n_heads, int num_splits, const uint16_t* o_partial,
                           const float* lse_partial, const uint16_t* w_uv, uint16_t* out, float* lse_out,

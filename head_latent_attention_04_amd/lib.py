@@ -23,6 +23,7 @@ ROW = D_C + D_ROPE
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_BAD_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH, MLA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
 NO_ALLOC_SCRATCH_BYTES = 16 << 20
+CHECK_BAD_LENGTH, CHECK_BAD_BLOCK, CHECK_BAD_OFFSETS, CHECK_CHUNK_TOO_LONG = 1, 2, 4, 8
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -61,6 +62,8 @@ EXPORTS = {
     "mla_chunked_prefill_expanded": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp,
                                                     _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "mla_kv_down_append_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32]),
+    "mla_check_inputs": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp, _i32, _vp,
+                                        _vp]),
     "mla_kv_down_query_absorbed_workspace_size": (_sz, [ctypes.POINTER(MlaDims), _i32, _i32, _i32]),
     "mla_kv_down_query_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaCache), _i32, _vp, _vp,
                                                   _vp, _i32, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_float,
@@ -285,6 +288,17 @@ def kv_down_append(dims: MlaDims, cache: MlaCache, token_seq, token_pos, x, w_dk
         _ptr(w_dkv, "w_dkv", BF16, (dims.d_c + dims.d_rope) * dim), _ptr(gamma, "gamma", BF16, dims.d_c), eps,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_kv_down_append", st)
+
+
+def check_inputs(dims: MlaDims, cache: MlaCache, seq_lens, error_word, cu_q_lens=None, total_q: int = 0,
+                 stream=None):
+    """mla_check_inputs: error_word (one int32 on the device) receives the MLA_CHECK_* bits of the rules
+    the lengths, block table and chunk offsets break (0: none)."""
+    B = seq_lens.numel()
+    st = load().mla_check_inputs(
+        ctypes.byref(dims), _cache(cache), B, _ptr(seq_lens, "seq_lens", I32, B),
+        _ptr(cu_q_lens, "cu_q_lens", I32, B + 1), total_q, _ptr(error_word, "error_word", I32, 1), _stream(stream))
+    _check("mla_check_inputs", st)
 
 
 def kv_down_query_absorbed_workspace_size(dims: MlaDims, num_tokens: int, dim: int, q_rank: int) -> int:

@@ -58,6 +58,13 @@ extern "C" {
 #define MLA_ERR_LAUNCH (-4)      /* the HIP runtime reported an error for a launch */
 #define MLA_ERR_TOO_LARGE (-5)   /* mla_decode_no_alloc: the call needs more than the static scratch holds */
 
+/* Bits of the error word mla_check_inputs writes (0: no rule broken). */
+#define MLA_CHECK_BAD_LENGTH 1      /* a seq_lens entry < 0 or > max_blocks_per_seq * block_size */
+#define MLA_CHECK_BAD_BLOCK 2       /* a block a sequence uses (logical block < ceil(len / block_size)) is
+                                       outside [0, num_blocks) */
+#define MLA_CHECK_BAD_OFFSETS 4     /* cu_q_lens is not 0 = cu[0] <= cu[1] <= ... <= cu[batch] = total_q */
+#define MLA_CHECK_CHUNK_TOO_LONG 8  /* a chunk has more new tokens than its sequence has tokens */
+
 /* Bytes of the static device scratch of mla_decode_no_alloc (one array per GPU, kept until exit). */
 #define MLA_NO_ALLOC_SCRATCH_BYTES (16u << 20)
 
@@ -358,6 +365,25 @@ int mla_query_absorbed(const mla_dims* dims, int32_t num_tokens, const int32_t* 
                        int32_t dim, const uint16_t* w_dq, const uint16_t* gamma_q, float eps, int32_t q_rank,
                        const uint16_t* w_q, void* workspace, size_t workspace_bytes, uint16_t* q_abs,
                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mla_check_inputs - a device-side check of the index data the other calls take on trust: the host
+ * cannot read device-resident lengths, block ids and chunk offsets, and the append and attention
+ * kernels address the cache with them ("论文复现工坊 No.4", section 2: the cache is addressed by
+ * sequence and position; the paged layout adds the block table of the descriptor above).
+ *   seq_lens   [batch] int32 (device): every sequence's length (as mla_decode / mla_chunked_prefill)
+ *   cu_q_lens  [batch + 1] int32 (device) or NULL: the chunk offsets of a prefill; NULL for decode
+ *   total_q    the prefill's total_q (ignored when cu_q_lens is NULL)
+ *   error_word [1] int32 (device, 4-byte aligned): written with the OR of the MLA_CHECK_* bits of the
+ *              rules the data breaks, 0 when it breaks none (batch == 0 writes 0)
+ * One work-group of one launch on `stream`; it reads seq_lens, the block table and cu_q_lens only
+ * (never the cache), so it is safe on bad data, allocates nothing, and can be captured in a graph.
+ * Cost grows with batch * max_blocks_per_seq (a debugging aid, not part of the hot path).
+ * Errors: MLA_ERR_NULL for a missing pointer (seq_lens when batch > 0, error_word), MLA_ERR_BAD_ARG
+ * for batch < 0, total_q < 0 with offsets, or a misaligned error_word; dims and cache as everywhere.
+ * ------------------------------------------------------------------------------------------- */
+int mla_check_inputs(const mla_dims* dims, const mla_cache* cache, int32_t batch, const int32_t* seq_lens,
+                     const int32_t* cu_q_lens, int32_t total_q, int32_t* error_word, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mla_kv_down_query_absorbed - mla_kv_down_append and mla_query_absorbed of the same new tokens in one

@@ -226,6 +226,21 @@ def test_kv_down_query_validation_and_workspace():
     assert lib.kv_down_query_absorbed_workspace_size(d, 32, 4096, 100) == 0
 
 
+def test_check_inputs_validation():
+    """mla_check_inputs' host checks: nothing is launched for a rejected call."""
+    d = D()
+    L = lib.load()
+    chk = lambda c=None, B=4, sl=FAKE, cu=None, tq=0, ew=FAKE, dims=d: L.mla_check_inputs(
+        ctypes.byref(dims), ctypes.byref(c if c is not None else cache()), B, sl, cu, tq, ew, None)
+    assert chk(ew=None) == lib.MLA_ERR_NULL
+    assert chk(sl=None) == lib.MLA_ERR_NULL
+    assert chk(B=-1) == lib.MLA_ERR_BAD_ARG
+    assert chk(cu=FAKE, tq=-1) == lib.MLA_ERR_BAD_ARG
+    assert chk(ew=FAKE + 2) == lib.MLA_ERR_BAD_ARG
+    assert chk(c=cache(data=None)) == lib.MLA_ERR_NULL
+    assert chk(dims=D(n_heads=120)) == lib.MLA_ERR_UNSUPPORTED
+
+
 MIS16 = FAKE + 8   # 8-byte aligned, not 16
 MIS8 = FAKE + 4    # 4-byte aligned, not 8
 MIS4 = FAKE + 2    # 2-byte aligned, not 4
