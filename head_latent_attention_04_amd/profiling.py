@@ -11,6 +11,11 @@
       prints the JSON that bench.py reads as the attention kernel's measured HBM traffic: the average
       FETCH_SIZE and WRITE_SIZE per dispatch of NAME, each scaled by the factor that turns the same
       counter's reading for a plain device copy of N bytes (read N, write N) into N bytes.
+
+  python3 -m head_latent_attention_04_amd.profiling backtoback <run_kernel_trace.csv> --kernel NAME
+      prints the average duration of the dispatches of NAME in the longest run of consecutive
+      dispatches of that kernel alone (a timing loop that launches it back to back), to set beside
+      a benchmark's per-launch figure for the same loop.
 """
 import argparse
 import csv
@@ -96,6 +101,24 @@ def counters(paths, kernel: str, command: str) -> str:
     return "\n".join(out)
 
 
+def backtoback(path: str, kernel: str) -> str:
+    """Longest run of consecutive dispatches (in dispatch order) whose kernel name contains `kernel`,
+    and the average, minimum and maximum duration of its dispatches in microseconds."""
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    best, cur = [], []
+    for r in rows:
+        if kernel in r["Kernel_Name"]:
+            cur.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            if len(cur) > len(best):
+                best = list(cur)
+        else:
+            cur = []
+    if not best:
+        raise SystemExit(f"no dispatch of {kernel}")
+    return (f"# {kernel}: longest back-to-back run {len(best)} dispatches, average {sum(best) / len(best):.2f} us "
+            f"(min {min(best):.2f}, max {max(best):.2f})")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="rocprofv3 summaries for profiles/")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -114,8 +137,13 @@ def main(argv=None):
     c.add_argument("csv", nargs="+")
     c.add_argument("--kernel", required=True)
     c.add_argument("--command", required=True)
+    d = sub.add_parser("backtoback")
+    d.add_argument("csv")
+    d.add_argument("--kernel", required=True)
     args = ap.parse_args(argv)
-    if args.cmd == "counters":
+    if args.cmd == "backtoback":
+        print(backtoback(args.csv, args.kernel))
+    elif args.cmd == "counters":
         print(counters(args.csv, args.kernel, args.command))
     elif args.cmd == "stats":
         print(stats(args.csv, args.title, args.command))
