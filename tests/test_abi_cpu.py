@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+from hypothesis import given, settings, strategies as hst
 
 from head_latent_attention_04_amd import lib
 
@@ -113,6 +114,24 @@ def test_plan_and_workspace_sizes():
     assert lib.decode_workspace_size(d, 32) == 32 * 128 * 576 * 2
     assert lib.decode_workspace_size(D(n_heads=120), 3) == 0
     assert lib.chunked_prefill_workspace_size(d, 2048) >= 2048 * 128 * 576 * 2
+
+
+@settings(max_examples=400, deadline=None)
+@given(batch=hst.integers(1, 5000), max_len=hst.integers(0, 1 << 20), cus=hst.integers(1, 1024))
+def test_decode_plan_properties(batch, max_len, cus):
+    """What the header states of mla_decode_plan, on random shapes: split_tokens is a positive multiple
+    of the block size, num_splits = ceil(max_seq_len / split_tokens) (1 for an empty batch of tokens),
+    so the splits cover every sequence and the last split is not empty; no more splits per sequence
+    than it takes to give every compute unit one work-group, and one split once the batch alone does."""
+    st_, ns = lib.decode_plan(D(), batch, max_len, cus)
+    assert st_ > 0 and st_ % 64 == 0 and ns >= 1
+    assert ns == (max(1, -(-max_len // st_)) if max_len > 0 else 1)
+    assert st_ * ns >= max_len and (max_len == 0 or (ns - 1) * st_ < max_len)
+    assert ns <= max(1, -(-cus // batch))
+    if batch >= cus:
+        assert ns == 1
+    if max_len > 0:
+        assert st_ <= -(-max_len // 64) * 64   # never longer than the longest sequence's blocks
 
 
 def kvd(dims, c, T=1, dim=4096, eps=1e-6, ptrs=(FAKE,) * 5, ws=FAKE, wsb=1 << 40):
