@@ -1,0 +1,96 @@
+"""A seeded sweep of random decode and prefill shapes against the fp64 oracle, on the GPU through the C
+ABI: head counts from 16 to 272 (one to three 128-head work-group groups, partial 32-head tiles),
+ragged lengths with block-edge values, contiguous and paged caches with spare blocks, the planner's
+split or a random split length, and chunks from one token to the whole sequence (and empty chunks in
+prefill). Every output and log-sum-exp is compared (gates of gpu_helpers); both prefill forms are run.
+
+Each case is drawn from its own seed (printed before it runs), and head count times cached tokens is
+kept at or below 200K so that the expanded oracle finishes each case in about a second.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (assert_close, assert_lse, decode_lse_of_rounded_query, oracle_cache,
+                         prefill_lse_of_rounded_query, run_decode, say)
+from head_latent_attention_04_amd.runner import DeviceCase, to_f64
+from oracle import mla_oracle as O
+from workloads import make_case
+
+pytestmark = pytest.mark.gpu
+
+HEADS = [16, 32, 48, 64, 96, 128, 144, 160, 272]
+BUDGET = 200_000          # n_heads x cached tokens per case
+LSE_EXPANDED = 1e-2       # the expanded form's lse against the exact one
+
+
+def _lengths(rng, H, B, hi):
+    lens = rng.integers(1, hi + 1, size=B)
+    for b in range(B):   # block edges: 1, 63, 64, 65, 127, 128, 129
+        if rng.random() < 0.3:
+            lens[b] = int(rng.choice([1, 63, 64, 65, 127, 128, 129]))
+    scale = min(1.0, BUDGET / (H * max(1, int(lens.sum()))))
+    return np.maximum(1, (lens * scale).astype(np.int64))
+
+
+def decode_case(seed):
+    rng = np.random.default_rng(seed)
+    H = HEADS[seed % len(HEADS)]   # consecutive seeds run every head count
+    B = int(rng.integers(1, 10))
+    lens = _lengths(rng, H, B, 3000)
+    paged = bool(rng.random() < 0.6)
+    spare = int(rng.integers(0, 4)) if paged else 0
+    st = None if rng.random() < 0.4 else 64 * int(rng.integers(1, 33))
+    return H, lens.tolist(), paged, spare, st
+
+
+def prefill_case(seed):
+    rng = np.random.default_rng(seed)
+    H = int(rng.choice(HEADS))
+    B = int(rng.integers(1, 5))
+    lens = _lengths(rng, H, B, 1500)
+    q = [int(rng.integers(0, min(int(L), 400) + 1)) if rng.random() < 0.8 else int(L) for L in lens]
+    if sum(q) == 0:
+        q[0] = 1
+    return H, lens.tolist(), q, bool(rng.random() < 0.6)
+
+
+DECODE_SEEDS = [9101 + i for i in range(10)]
+PREFILL_SEEDS = [9201, 9202, 9203, 9204, 9205, 9206, 9214, 9216, 9218]   # 9214: an empty chunk; 9218: 272 heads
+
+
+@pytest.mark.parametrize("seed", DECODE_SEEDS)
+def test_random_decode_shape(seed):
+    H, lens, paged, spare, st = decode_case(seed)
+    ns = None if st is None else -(-max(lens) // st)
+    say(f"[random decode] seed {seed}: H={H} lens={lens} paged={paged} spare={spare} split={st}x{ns}")
+    case = make_case(f"rand{seed}", seed, H, lens, paged=paged, spare_blocks=spare)
+    _, out, lse = run_decode(case, st, ns)
+    cache, q_rot = oracle_cache(case)
+    ref, rl = O.decode(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.q_nope, q_rot,
+                       case.w_uk, case.w_uv)
+    assert_close(out, ref, f"decode seed {seed}")
+    assert_lse(lse, rl, decode_lse_of_rounded_query(case, cache, q_rot), f"decode seed {seed}")
+
+
+@pytest.mark.parametrize("seed", PREFILL_SEEDS)
+def test_random_prefill_shape(seed):
+    H, lens, q, paged = prefill_case(seed)
+    say(f"[random prefill] seed {seed}: H={H} lens={lens} chunks={q} paged={paged}")
+    case = make_case(f"randp{seed}", seed, H, lens, q_lens=q, paged=paged, spare_blocks=1 if paged else 0)
+    dc = DeviceCase(case)
+    dc.fill_history()
+    dc.append_new()
+    dc.alloc_prefill()
+    dc.prefill()
+    dc.alloc_prefill_expanded()
+    dc.prefill_expanded()
+    torch.cuda.synchronize()
+    cache, q_rot = oracle_cache(case)
+    ref, rl = O.prefill(cache, case.block_table, case.max_blocks_per_seq, case.seq_lens, case.cu_q_lens,
+                        case.q_nope, q_rot, case.w_uk, case.w_uv)
+    assert_close(to_f64(dc.out), ref, f"absorbed prefill seed {seed}")
+    assert_lse(dc.lse.cpu().numpy().astype(np.float64), rl, prefill_lse_of_rounded_query(case, cache, q_rot),
+               f"absorbed prefill seed {seed}")
+    assert_close(to_f64(dc.out_x), ref, f"expanded prefill seed {seed}")
+    assert np.max(np.abs(dc.lse_x.cpu().numpy().astype(np.float64) - rl)) <= LSE_EXPANDED
