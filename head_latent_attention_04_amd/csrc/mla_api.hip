@@ -1,6 +1,7 @@
 // C ABI of the MLA library: host-side validation, workspace layout and kernel launches.
 // Every check happens before the first HIP call, so an invalid call enqueues nothing.
 #include <math.h>
+#include <algorithm>
 #include <stddef.h>
 
 #include <mutex>
@@ -79,17 +80,31 @@ hipError_t device_scratch(void** ptr) {
   return hipSuccess;
 }
 
+// Splits of each absorbed-prefill row's causal key range. One while the (row, 128-head group)
+// work-groups fill the compute units; with fewer than kPrefillSplitCus of them, as many splits as
+// still fit in one wave of work-groups on that many units (at most kMaxPrefillSplits): rounding up
+// would start a second, mostly idle wave. A function of n_heads and total_q only, so the workspace
+// size query knows it.
+constexpr int64_t kPrefillSplitCus = 256;
+constexpr int64_t kMaxPrefillSplits = 8;
+
+int prefill_splits(int32_t n_heads, int32_t total_q) {
+  const int64_t wgs = (int64_t)(total_q > 0 ? total_q : 0) * ((mla::q_tiles(n_heads) + 3) / 4);
+  if (wgs <= 0 || wgs >= kPrefillSplitCus) return 1;
+  return (int)std::min<int64_t>(kMaxPrefillSplits, kPrefillSplitCus / wgs);
+}
+
 struct PrefillWorkspace {
   size_t q_abs, o_lat, lse, total;
 };
 
 PrefillWorkspace prefill_layout(const mla_dims* d, int32_t total_q) {
   PrefillWorkspace w;
-  size_t rows = (size_t)(total_q > 0 ? total_q : 0) * (size_t)d->n_heads;
+  const size_t parts = (size_t)(total_q > 0 ? total_q : 0) * (size_t)d->n_heads * prefill_splits(d->n_heads, total_q);
   w.q_abs = 0;
   w.o_lat = align256((size_t)(total_q > 0 ? total_q : 0) * mla::q_tiles(d->n_heads) * mla::kQTileElems * 2);
-  w.lse = w.o_lat + align256(rows * mla::kDc * 2);
-  w.total = w.lse + align256(rows * 4);
+  w.lse = w.o_lat + align256(parts * mla::kDc * 2);
+  w.total = w.lse + align256(parts * 4);
   return w;
 }
 
@@ -338,8 +353,9 @@ int mla_decode_plan(const mla_dims* dims, int32_t batch, int32_t max_seq_len, in
 // new tokens after 8192: the absorbed attention sustains 1.15 PFLOP/s, the expanded form's
 // up-projection 0.80 and its attention 0.91; the absorbed form's absorption and combine cost about
 // 0.12 us per query row; each form about 20 us of launches). The absorbed attention runs one
-// work-group per query row (per 128 heads), so fewer rows than compute units leave units idle; the
-// expanded form up-projects every cached token in 256-token tiles and attends in 256-query tiles.
+// work-group per query row (per 128 heads) and split (prefill_splits), and counts whole waves of
+// work-groups on the compute units; the expanded form up-projects every cached token in 256-token
+// tiles and attends in 256-query tiles.
 int mla_chunked_prefill_plan(const mla_dims* dims, int32_t batch, const int32_t* seq_lens, const int32_t* q_lens,
                              int32_t num_cus, int32_t* use_expanded, float* absorbed_us, float* expanded_us) {
   int st = check_dims(dims);
@@ -362,7 +378,7 @@ int mla_chunked_prefill_plan(const mla_dims* dims, int32_t batch, const int32_t*
     rows += q;
   }
   const int groups = (mla::q_tiles(dims->n_heads) + 3) / 4;
-  const double wg = rows * groups;
+  const double wg = rows * groups * prefill_splits(dims->n_heads, (int32_t)std::min(rows, (double)kMaxPrefillTokens));
   const double wave_factor = wg > 0 ? ceil(wg / num_cus) * num_cus / wg : 1.0;
   const double t_abs = pairs * H * 2 * (mla::kRow + mla::kDc) / kAbsorbedRate * 1e6 * wave_factor + kPerRowUs * rows +
                        kLaunchUs;
@@ -534,13 +550,23 @@ int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t ba
   // many rows: the absorbed queries in the plain layout, which the absorption writes in whole lines
   hipError_t e = mla::launch_absorb(total_q, dims->n_heads, q_nope, q_rope, w_uk, q_abs, true, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
-  // one query token per row; the whole causal key range of a row is one split (split_tokens is
-  // only the split length, so any multiple of the block covering the longest sequence works)
+  // one query token per row. With enough rows the whole causal key range of a row is one split
+  // (split_tokens only bounds a split, so the largest block multiple covers any sequence). With few
+  // rows the range is cut into prefill_splits pieces of the descriptor's capacity (max_blocks_per_seq
+  // blocks bound every length), each a block multiple; splits past a row's length stay empty.
   (void)max_q_len;
+  int32_t split_tokens = kMaxSplitTokens, num_splits = 1;
+  const int splits = prefill_splits(dims->n_heads, total_q);
+  const int64_t cap = (int64_t)cache->max_blocks_per_seq * dims->block_size;
+  if (splits > 1 && cap <= ((int64_t)1 << 30)) {
+    const int64_t bs = dims->block_size;
+    split_tokens = (int32_t)(((cap + splits - 1) / splits + bs - 1) / bs * bs);
+    num_splits = (int32_t)((cap + split_tokens - 1) / split_tokens);  // <= splits
+  }
   e = mla::launch_attention(view(cache), total_q, dims->n_heads, seq_lens, cu_q_lens, batch, q_abs, false, dims->scale,
-                            kMaxSplitTokens, 1, o_lat, lse, stream);
+                            split_tokens, num_splits, o_lat, lse, stream);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
-  return launched(mla::launch_combine(total_q, dims->n_heads, 1, o_lat, lse, w_uv, out, lse_out, stream));
+  return launched(mla::launch_combine(total_q, dims->n_heads, num_splits, o_lat, lse, w_uv, out, lse_out, stream));
 }
 
 }  // extern "C"

@@ -289,6 +289,10 @@ size_t mla_chunked_prefill_workspace_size(const mla_dims* dims, int32_t total_q)
  *   w_uk, w_uv as for decode;  out [total_q, n_heads, d_v] bf16;  lse_out [total_q, n_heads] fp32 or NULL
  *   workspace >= mla_chunked_prefill_workspace_size(dims, total_q) bytes, 256-byte aligned
  *   total_q <= 16777216; q_nope, q_rope, w_uk, w_uv 16-byte aligned, out 8-byte aligned
+ * Three launches (absorption, attention, combine with W_UV). With fewer than 256 (query row,
+ * 128-head group) pairs the attention splits each row's keys into up to 8 pieces of the cache
+ * descriptor's capacity (max_blocks_per_seq * block_size, rounded to blocks) so the work covers more
+ * compute units, and the combine merges them; the workspace size accounts for it.
  * ------------------------------------------------------------------------------------------- */
 int mla_chunked_prefill(const mla_dims* dims, const mla_cache* cache, int32_t batch,
                         const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t total_q,

@@ -114,6 +114,11 @@ def test_plan_and_workspace_sizes():
     assert lib.decode_workspace_size(d, 32) == 32 * 128 * 576 * 2
     assert lib.decode_workspace_size(D(n_heads=120), 3) == 0
     assert lib.chunked_prefill_workspace_size(d, 2048) >= 2048 * 128 * 576 * 2
+    # few rows: each row's keys in floor(256 / rows) splits (at most 8), partials and lse per split
+    for rows, splits in ((64, 4), (100, 2), (20, 8), (256, 1), (300, 1)):
+        need = rows * 128 * 576 * 2 + rows * 128 * splits * (512 * 2 + 4)
+        assert lib.chunked_prefill_workspace_size(d, rows) >= need
+        assert lib.chunked_prefill_workspace_size(d, rows) < need + rows * 128 * (512 * 2 + 4) + 3 * 256
 
 
 @settings(max_examples=400, deadline=None)
