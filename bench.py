@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", choices=["decode", "decode_configs", "prefill", "prefill_crossover", "kv_down", "query",
-                                           "output", "layer"],
+                                           "output", "layer", "mfma_ceiling"],
                     default="decode",
                     help="decode: B=32, n_h=128, 4K context (the headline); decode_configs: the same decode step "
                          "on the ragged paged batch (B=64, lengths 512..32768) and on the long context (B=4, "
@@ -58,7 +58,8 @@ def parse():
                          "step's output side, W_UV folded into wo against combine + wo, 32 tokens, width 4096; layer: one decode "
                          "layer of the attention from the hidden state (kv_down_query_absorbed, attention, combine, wo; "
                          "the separate kv_down_append + query_absorbed calls timed beside), B=32, 4096 cached tokens, "
-                         "width 4096")
+                         "width 4096; mfma_ceiling: the sustained bf16 MFMA rate and shader clock of a register-operand "
+                         "probe on random, zero and constant operands, one 4-wave work-group per compute unit")
     return ap.parse_args()
 
 
@@ -226,6 +227,8 @@ def main():
         return output_main(args, torch, lib, props)
     if args.workload == "layer":
         return layer_main(args, torch, lib, props)
+    if args.workload == "mfma_ceiling":
+        return mfma_ceiling_main(args, torch, lib, props)
     case = make_config(1)
     B, H = case.batch, case.n_heads
     L = int(case.seq_lens[0])
@@ -592,6 +595,65 @@ def crossover_main(args, torch, lib, props):
         "data": "synthetic",
         "config": {"workload": f"chunked prefill B=2 n_h={H}, {prefix} cached + chunk q, causal", "prefix": prefix},
         "sweep": rows, "device": props.name,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def mfma_ceiling_main(args, torch, lib, props):
+    """The rate at which the chip sustains v_mfma_f32_32x32x16_bf16 work and the shader clock it runs at
+    (the probe of head_latent_attention_04_amd/probe, its own library), for random bf16 operands (the
+    kind of data the attention kernels multiply), all-zero operands and one constant value, with one
+    4-wave work-group per compute unit as the attention kernel runs. Each launch lasts milliseconds,
+    long enough for the clock to settle under the load."""
+    import ctypes
+
+    from head_latent_attention_04_amd.build import PROBE_LIB
+
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: run __graft_entry__.build() first")
+    plib = ctypes.CDLL(PROBE_LIB)
+    plib.mla_probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    plib.mla_probe_mfma_rate.restype = ctypes.c_int
+    plib.mla_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    plib.mla_probe_mfma_flops.restype = ctypes.c_double
+    blocks, iters = props.multi_processor_count, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    variants = {
+        "random": torch.randn(8 * 64 * 8, generator=gen).to(torch.bfloat16).view(torch.int16),
+        "zero": torch.zeros(8 * 64 * 8, dtype=torch.int16),
+        "constant": torch.full((8 * 64 * 8,), 0x3F80, dtype=torch.int16),   # bf16 1.0
+    }
+    flops = plib.mla_probe_mfma_flops(blocks, iters)
+    out = {}
+    for name, host in variants.items():
+        ops = host.to("cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def run(i):
+            rc = plib.mla_probe_mfma_rate(ops.data_ptr(), blocks, iters, sink.data_ptr(), stamps.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+
+        for i in range(2):
+            run(i)
+        ms = time_each(torch, run, 5)
+        st = stamps.view(-1, 2).cpu().numpy().astype(np.float64)
+        clock = float(st[:, 0].sum() / st[:, 1].sum() * 0.1)   # shader clock counts per 100 MHz count
+        out[name] = {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "ms_per_launch": round(ms, 4),
+                     "shader_clock_GHz": round(clock, 3)}
+    rnd = out["random"]["TFLOP/s"]
+    result = {
+        "metric": "sustained bf16 MFMA rate of a register-operand probe, random operands",
+        "value": rnd, "unit": "TFLOP/s", "n_gpus": 1, "steps": 5, "warmup": 2, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"v_mfma_f32_32x32x16_bf16 chains, {blocks} work-groups x 4 waves, {iters} x 16 MFMAs "
+                               "per wave, operand registers rotating"},
+        "roofline": {"bound": "mfma", "achieved": rnd, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(rnd / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "variants": out, "device": props.name,
     }
     print(json.dumps(result), flush=True)
 

@@ -3,8 +3,9 @@
     python -m head_latent_attention_04_amd.build
 
 Every HIP source under csrc/ is compiled to an object file, then all are linked into one
-shared library next to this file. Packed-FP32 instruction selection is disabled for all
-device code.
+shared library next to this file. The measurement probe under probe/ (not part of the attention
+path; bench.py's mfma_ceiling workload runs it) is built into a library of its own,
+libmla_probe.so. Packed-FP32 instruction selection is disabled for all device code.
 """
 from __future__ import annotations
 
@@ -20,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_rate.hip")
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")
 ARCH = "gfx950"
 
 
@@ -59,9 +62,21 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources, and {PROBE_LIB}")
     return LIB
+
+
+def build_probe() -> str:
+    """The MFMA-rate probe as its own shared library (bench.py --workload mfma_ceiling)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *common_flags(), "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def asan_runtime() -> str:

@@ -385,3 +385,13 @@ def test_chunked_prefill_plan_follows_the_measured_crossover():
     assert L.mla_chunked_prefill_plan(C.byref(d), 1, (C.c_int32 * 1)(4), bad, 256, C.byref(out), None, None) \
         == lib.MLA_ERR_BAD_ARG  # chunk longer than the sequence
     assert L.mla_chunked_prefill_plan(C.byref(d), 0, None, None, 256, C.byref(out), None, None) == lib.MLA_OK
+
+
+def test_probe_library_exports_its_symbols():
+    from head_latent_attention_04_amd.build import PROBE_LIB
+    probe = ctypes.CDLL(PROBE_LIB)
+    for name in ("mla_probe_mfma_rate", "mla_probe_mfma_flops"):
+        assert hasattr(probe, name)
+    probe.mla_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.mla_probe_mfma_flops.restype = ctypes.c_double
+    assert probe.mla_probe_mfma_flops(256, 10) == 256 * 4 * 10 * 16 * 2 * 32 * 32 * 16
