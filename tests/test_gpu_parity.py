@@ -14,7 +14,7 @@ from gpu_helpers import (SCALE, assert_close, assert_lse, decode_lse_of_rounded_
 from head_latent_attention_04_amd import lib
 from head_latent_attention_04_amd.runner import DeviceCase, to_f64
 from oracle import mla_oracle as O
-from workloads import BF16_NAN, make_case
+from workloads import BF16_NAN, bf16_bits, make_case
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,38 @@ def test_rope_append_large_positions():
     ref, _ = O.rope_append(ref, None, case.max_blocks_per_seq, case.token_seq[idx], case.token_pos[idx],
                            case.c_kv[idx], case.k_rope[idx])
     assert np.array_equal(got, ref)
+
+
+def test_rope_append_positions_near_2_20():
+    """Positions 2^20 - 300 .. 2^20 - 1 (a million-token context) through a paged table of 16384
+    entries that maps only the blocks the tokens land in (every other entry points at one spare,
+    poisoned block): the cache rows and the rotated queries stay bit-exact (angles formed in fp64)."""
+    say("[rope_append] positions near 2^20")
+    rng = np.random.Generator(np.random.PCG64(77))
+    T, H, top = 300, 16, 1 << 20
+    pos = np.arange(top - T, top, dtype=np.int32)
+    seq = np.zeros(T, np.int32)
+    max_blocks = top // 64
+    used = np.unique(pos // 64)
+    num_blocks = len(used) + 1
+    table = np.full((1, max_blocks), num_blocks - 1, np.int32)
+    table[0, used] = rng.permutation(len(used)).astype(np.int32)
+    c_kv = bf16_bits(rng.standard_normal((T, 512)))
+    k_rope = bf16_bits(rng.standard_normal((T, 64)))
+    q_rope = bf16_bits(rng.standard_normal((T, H, 64)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to("cuda")
+    data = torch.full((num_blocks, 64, 576), BF16_NAN, dtype=torch.int16, device="cuda")
+    table_d = dev(table)
+    cache = lib.make_cache(data, table_d, max_blocks)
+    q_d = dev(q_rope)
+    lib.rope_append(lib.make_dims(H), cache, dev(seq), dev(pos), dev(c_kv), dev(k_rope), q_d)
+    torch.cuda.synchronize()
+    ref = np.full((num_blocks, 64, 576), BF16_NAN, np.uint16)
+    ref, _ = O.rope_append(ref, table, max_blocks, seq, pos, c_kv, k_rope)
+    got = data.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} cache elements differ"
+    q_ref = O.f64_to_bf16(O.rope_rotate(O.bf16_to_f64(q_rope), pos[:, None]))
+    assert np.array_equal(q_d.cpu().numpy().view(np.uint16), q_ref)
 
 
 def test_partials_and_combine_match_oracle():
