@@ -134,8 +134,10 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
       }
       // Lane (row, kh) holds columns 8 q + 4 kh .. +3 of its row. For each pair of groups (q, q+1) the
       // lanes l and l ^ 32 trade halves so that the low lane writes group q and the high lane group
-      // q+1 as whole 16-byte pieces (8 consecutive columns, one operand-order chunk): each lane sends
-      // the half its partner is missing.
+      // q+1 as whole 16-byte pieces (8 consecutive columns, one operand-order chunk). v_permlane32_swap
+      // (x, y) leaves the low lane its own x and the high lane's x, and the high lane the low lane's y
+      // and its own y, so with x = group q and y = group q+1 both lanes read their piece in the same
+      // order.
       uint32_t w[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -144,10 +146,9 @@ __device__ __forceinline__ void absorb_tile(int h, int ch, int rbase, int rows, 
       }
 #pragma unroll
       for (int q = 0; q < 4; q += 2) {
-        const uint32_t t0 = __shfl_xor(kh ? w[2 * q] : w[2 * q + 2], 32);
-        const uint32_t t1 = __shfl_xor(kh ? w[2 * q + 1] : w[2 * q + 3], 32);
-        const uint4 v = kh == 0 ? make_uint4(w[2 * q], w[2 * q + 1], t0, t1)
-                                : make_uint4(t0, t1, w[2 * q + 2], w[2 * q + 3]);
+        const auto r0 = __builtin_amdgcn_permlane32_swap(w[2 * q], w[2 * q + 2], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(w[2 * q + 1], w[2 * q + 3], false, false);
+        const uint4 v = make_uint4(r0[0], r1[0], r0[1], r1[1]);
         const int d = ch * kCols + cb + 8 * (q + kh);
         if (r < rows) *reinterpret_cast<uint4*>(q_abs + out_off(r, d)) = v;
       }

@@ -141,6 +141,17 @@ __device__ __forceinline__ const uint16_t* block_base(const CacheView& c, int se
   return c.data + phys * (int64_t)(kBlock * kRow);
 }
 
+// max and sum of a value over the lane pair (l, l ^ 32), returned to both lanes: v_permlane32_swap
+// trades the two halves in registers (a shuffle through ds_bpermute would wait on the LDS queue)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x4_lo(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
@@ -425,7 +436,7 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
         }
         mx = fmaxf(mx, sc[e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      mx = pair_max(mx) * scale_log2;
       if (__any(mx > m_ref + kRescaleExcess)) {
         const float mn = fmaxf(m_ref, mx);
         const float f = exp2f(m_ref - mn);  // 0 on the first tile (m_ref = -inf)
@@ -466,7 +477,7 @@ __global__ void __launch_bounds__(512) expanded_attn_kernel(CacheView cache, con
   if (!w_live) return;
 
   // out[j, h, d] = O / l; lanes l and l ^ 32 hold the same query (different keys and value rows)
-  const float tot = lsum + __shfl_xor(lsum, 32);
+  const float tot = pair_sum(lsum);
   const float inv = 1.f / tot;
   const int jl = w_first + (lane & 31);
   if (jl >= qlen) return;
