@@ -11,7 +11,7 @@ accumulation over `dim` products and an fp32 reciprocal square root) against a b
 the projection's rounding flips, the element moves by one bf16 step of kv and then by one more
 rounding step of the normalised or rotated value, so no element may move by more than
 2^-6 max(1, |ref|) (two bf16 steps; the floor of 1 covers the rotation's cancellation, where a
-rotated pair's output is smaller than its inputs). The benchmark spec's relative Frobenius gate (5e-3)
+rotated pair's output is smaller than its inputs). The attention output's relative Frobenius gate (5e-3)
 is applied on top, per part (c_KV, k_R).
 """
 import numpy as np

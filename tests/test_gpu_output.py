@@ -4,7 +4,7 @@ mla_fold_output_weights, mla_output_projection) with the fp64 oracle, on the GPU
 Weight preparation is a permutation (checked bit for bit). Sums run in fp32 where the oracle uses
 fp64 and are rounded once to bf16, so an output may land one bf16 step away from the oracle's; where
 a sum nearly cancels, the fp32 error is measured against the typical output size. Gates: relative
-Frobenius error <= 5e-3 (the benchmark spec's), every element within one bf16 step of
+Frobenius error <= 5e-3 (the attention output's gate), every element within one bf16 step of
 max(|ref|, rms(ref)), at least 95% bit-identical. The merge is checked on host-drawn partials with
 the combine's tolerance (relative Frobenius 5e-3, max abs 2e-2, lse 1e-2).
 """

@@ -4,7 +4,7 @@ mla_query_absorbed) with the fp64 oracle, on the GPU.
 The kernels accumulate in fp32 where the oracle uses fp64, and the compressed query c_q is rounded
 to bf16 between the two projections, so an output can land one bf16 step away from the oracle's
 (and, where c_q itself rounded the other way, a second step: the perturbation is one bf16 step of
-one of q_rank terms). Gates per output part: relative Frobenius error <= 5e-3 (the benchmark spec's),
+one of q_rank terms). Gates per output part: relative Frobenius error <= 5e-3 (the attention output's gate),
 no element off by more than 2^-6 max(1, |ref|) (two bf16 steps), and at least 90% of the elements
 bit-identical. The weight product alone (fp32 sums of 128 products against fp64) must be >= 99%
 bit-identical and within one step plus the fp32 summation bound of the reference.
