@@ -103,3 +103,21 @@ def test_kv_down_append_prefill_chunk_full_size():
     """The chunked prefill's new tokens: 2 x 1024 after 8192 cached, width 4096."""
     say("[kv_down_append] prefill chunk: 2048 tokens, dim 4096")
     run_case([9216, 9216], [1024, 1024], 4096, seed=12)
+
+
+def _random_kv_case(seed):
+    """1-5 sequences of 1-2999 cached tokens, each appending 1-300 of them (so both the split-K path
+    below 256 tokens and the tiled one above), at a width from 64 to 4096."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 6))
+    lens = rng.integers(1, 3000, B)
+    new = [int(rng.integers(1, min(int(L), 300) + 1)) for L in lens]
+    dim = int(rng.choice([64, 192, 320, 512, 1024, 2048, 4096]))
+    return lens.tolist(), new, dim
+
+
+@pytest.mark.parametrize("seed", list(range(300, 320)))
+def test_kv_down_append_random_shapes(seed):
+    lens, new, dim = _random_kv_case(seed)
+    say(f"[kv_down_append] seed {seed}: lens={lens} new={new} dim={dim}")
+    run_case(lens, new, dim, seed=seed)

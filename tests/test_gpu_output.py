@@ -160,3 +160,21 @@ def test_output_folded_matches_oracle(H, T, dim, device_weights):
     lib.output_projection(dims, o_d, w_d, dim, True, ws, y)
     torch.cuda.synchronize()
     compare(y.cpu().numpy().view(np.uint16)[:, rows], O.output_folded(inp.o_lat, ref_w), "y folded")
+
+
+@pytest.mark.parametrize("seed", list(range(500, 520)))
+def test_output_projection_random_shapes(seed):
+    """wo on the flattened heads for 16-128 heads, 1-99 rows, width 64-4096."""
+    rng = np.random.default_rng(seed)
+    H = int(rng.choice([16, 32, 48, 64, 128]))
+    T = int(rng.integers(1, 100))
+    dim = int(rng.choice([64, 192, 320, 512, 1024, 2048, 4096]))
+    say(f"[output] seed {seed}: wo H={H} T={T} dim={dim}")
+    inp = make_output_inputs(seed, T, dim, H)
+    dims = lib.make_dims(H)
+    out_d, w_d = _dev(inp.out), _dev(operand_order(inp.w_o))
+    ws = torch.empty(lib.output_projection_workspace_size(dims, T, dim, False), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, dim), dtype=torch.int16, device="cuda")
+    lib.output_projection(dims, out_d, w_d, dim, False, ws, y)
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy().view(np.uint16), O.output_projection(inp.out, inp.w_o), "y")

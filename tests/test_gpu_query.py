@@ -126,3 +126,24 @@ def test_query_absorbed_with_device_prepared_weights():
     got, ref = run_query(128, 32, 4096, 512, [4095] * 32, seed=24, w_uqk_bits=True)
     compare(got[..., :512], ref[..., :512], "q_abs latent part", 0.90)
     compare(got[..., 512:], ref[..., 512:], "q_R part", 0.90)
+
+
+def _random_query_case(seed):
+    """16-144 heads, 1-99 tokens at positions below 2^20, width 64-4096, rank 64-1536."""
+    rng = np.random.default_rng(seed)
+    H = int(rng.choice([16, 32, 48, 64, 96, 128, 144]))
+    T = int(rng.integers(1, 100))
+    dim = int(rng.choice([64, 192, 320, 512, 1024, 2048, 4096]))
+    q_rank = int(rng.choice([64, 128, 192, 256, 512, 1024, 1536]))
+    pos = rng.integers(0, 1 << 20, T)
+    return H, T, dim, q_rank, pos
+
+
+# seeds of the generator whose fp64 oracle runs in under 2 s
+@pytest.mark.parametrize("seed", [401, 405, 406, 407, 408, 409, 413, 417, 421, 422, 423, 424, 425, 426, 428, 429])
+def test_query_absorbed_random_shapes(seed):
+    H, T, dim, q_rank, pos = _random_query_case(seed)
+    say(f"[query absorbed] seed {seed}: H={H} T={T} dim={dim} q_rank={q_rank}")
+    got, ref = run_query(H, T, dim, q_rank, pos, seed=seed)
+    compare(got[..., :512], ref[..., :512], "q_abs latent part", 0.90)
+    compare(got[..., 512:], ref[..., 512:], "q_R part", 0.90)
