@@ -346,21 +346,10 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, src[64 * ks]);
     } else {
-      // Plain rows [row, head, 576]: the tile's 32 rows are one contiguous 36 KB block. Each load
-      // instruction reads 64 consecutive 16-byte chunks of one half of the rows (dims 288 p .. +287),
-      // i.e. a few whole lines, instead of 16-byte pieces of 32 rows; the halves then pass through
-      // this wave's 18 KB of the stage buffers 2 and 3 (idle until step 0 copies stage 2) and are read
-      // back in operand order. qreg[18 p + i] holds load i of half p until it is written to LDS.
-      // Heads past n_heads read the last head's row, as the operand-order form does.
+      const int hq = min(32 * tile + n, n_heads - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(q_abs + ((int64_t)qrow * n_heads + hq) * kRow + 8 * kh);
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int i = 0; i < 18; ++i) {
-          const int lin = 64 * i + lane;  // chunk lin of half p: row lin / 36, chunk lin % 36 of the half
-          const int hq = min(32 * tile + lin / 36, n_heads - 1);
-          qreg[18 * p + i] = __builtin_bit_cast(
-              bf16x8, reinterpret_cast<const uint4*>(q_abs + ((int64_t)qrow * n_heads + hq) * kRow + 288 * p)[lin % 36]);
-        }
+      for (int ks = 0; ks < 36; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
     }
   }
 
@@ -373,27 +362,6 @@ __device__ __forceinline__ void attend_tile(const CacheView& cache, int n_heads,
   // first step needs anyway) and knows the query is resident inside the loop; otherwise it would
   // guard each score MFMA with a wait that also drains the copies in flight. Stage 1 follows.
   issue_stage<kNt>(block_ptr(cache, b, blk0), 0, lds0, min(kStageTok, t1 - t0), wave, lane);
-  if constexpr (!kOperandOrder) {
-    // LDS image of a half: row r (0..31) at 576 r, its chunk c at 16 (c ^ ((r >> 2) & 3)), so the
-    // operand reads (16 rows at one chunk per 16-lane group) fall on 16 distinct 16-byte bank groups
-    lds_char* qs = lds + 2 * kStageBytes + wave * (32 * kRow);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const int lin = 64 * i + lane, r = lin / 36, c = lin % 36;
-        *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(qs + r * kRow + 16 * (c ^ ((r >> 2) & 3))) =
-            qreg[18 * p + i];
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const int c = 2 * i + kh;
-        qreg[18 * p + i] = lds_b128(qs + n * kRow + 16 * (c ^ ((n >> 2) & 3)));
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-  }
   asm volatile("" ::"v"(qreg[35]));
   if (nstages > 1)
     issue_stage<kNt>(block_ptr(cache, b, blk0), 1, lds0 + kStageBytes, min(kStageTok, t1 - t0 - kStageTok), wave,
